@@ -1,0 +1,57 @@
+// Device helpers shared by the HIP kernels of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pps {
+
+// bf16 <-> fp32.  bf16 is the upper half of an IEEE fp32 word; conversion
+// to bf16 rounds to nearest, ties to even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+__device__ __forceinline__ uint32_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Round an fp32 value to the nearest bf16 value, returned as fp32.
+__device__ __forceinline__ float round_bf(float f) { return bf2f(f2bf(f)); }
+
+template <typename S> struct Store;
+template <> struct Store<uint16_t> {
+    static __device__ __forceinline__ float load(const uint16_t* p) { return bf2f(*p); }
+    static __device__ __forceinline__ void store(uint16_t* p, float v) { *p = (uint16_t)f2bf(v); }
+    static __device__ __forceinline__ float round(float v) { return round_bf(v); }
+};
+template <> struct Store<float> {
+    static __device__ __forceinline__ float load(const float* p) { return *p; }
+    static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+    static __device__ __forceinline__ float round(float v) { return v; }
+};
+
+__device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+// h = silu(g) * u with silu(g) = g * sigmoid(g).
+__device__ __forceinline__ float swiglu_f(float g, float u) { return g * sigmoid_f(g) * u; }
+
+// Gradient of h = silu(g) u: du = dh silu(g); dg = dh u s (1 + g (1 - s)).
+__device__ __forceinline__ void swiglu_bwd_f(float dh, float g, float u, float& dg, float& du) {
+    const float s = sigmoid_f(g);
+    du = dh * g * s;
+    dg = dh * u * s * (1.0f + g * (1.0f - s));
+}
+
+// Exact (erf-based) GELU and its derivative Phi(z) + z phi(z).
+__device__ __forceinline__ float gelu_f(float z) {
+    return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+__device__ __forceinline__ float gelu_grad_f(float z) {
+    const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
+    const float pdf = 0.39894228040143268f * expf(-0.5f * z * z);
+    return cdf + z * pdf;
+}
+
+}  // namespace pps

@@ -1,0 +1,737 @@
+// The stage executor behind the C ABI: call validation against the stage's
+// schedule, the preallocated activation stash, and the per-op kernel
+// sequences.
+//
+// Page legend: [1F1B] "2. 1F1B"; [GPipe->ZB] "流水线并行：从 GPipe 到 1F1B 与
+// Zero Bubble"; [Sched] "流水线调度：GPipe、1F1B、交错与计算通信重叠";
+// [Megatron-PP] "Megatron-LM 分布式训练（三）：流水线并行 PP 与 1F1B 调度".
+//
+// The stash plays the role of the per-stage activations dict of [1F1B §5.2]:
+// a forward stores what its backward needs, the backward takes the entry
+// out and releases it, and the number of live entries is the in-flight count
+// ([1F1B §4.1]).  Entries live in a pool of S fixed-size slots allocated once
+// at create ([1F1B §5.3]: reuse buffers instead of allocating per message);
+// S is the schedule's peak live count (P-k for 1F1B, M for GPipe).
+//
+// SwiGLU block b of an entry keeps x [T,d], r [T] (fp32), g and u [T,ffn].
+// With the Zero-Bubble split ([GPipe->ZB Zero Bubble]: B = dX now, W = dW
+// later, X and G stay resident until W) the entry also keeps dg|du [T,2ffn]
+// and dy [T,d] per block after B, until W.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kernels.h"
+#include "schedule_internal.h"
+
+namespace {
+
+using pps::GemmArgs;
+
+constexpr int ST_NONE = 0, ST_F = 1, ST_B = 2, ST_W = 3;
+
+inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct Layout {
+    // offsets inside one slot, per block (index b)
+    std::vector<size_t> x, r, g, u, dgu, dy, z, dz;
+    size_t fwd_bytes = 0;     // bytes an entry uses before B
+    size_t split_bytes = 0;   // extra bytes kept from B until W
+    size_t slot_bytes = 0;
+};
+
+}  // namespace
+
+struct pps_stage {
+    pps_stage_desc d{};
+    std::vector<const void*> w;
+    bool bookkeeping = false, profile = false, split = false, swiglu = true;
+    int es = 2;                       // element size of the storage dtype
+    int nw = 4;                       // weights per block
+    int S = 0;                        // slots
+    std::vector<pps_op> sched;
+    std::vector<std::pair<int, int>> fseq, bseq, wseq;   // (mb, chunk) per kind, in order
+    std::vector<int> tf, tb, tw;                          // t_start per kind entry
+    size_t fpos = 0, bpos = 0, wpos = 0;
+    std::vector<int> status, slot_of;                     // [chunk*M + mb]
+    std::vector<char> slot_used;
+    int live = 0;
+    int64_t live_bytes = 0;
+    std::vector<pps_op> oplog;
+    pps_stats st{};
+    bool failed = false;
+
+    hipStream_t stream = nullptr;
+    Layout lay;
+    char* pool = nullptr;
+    char* scratch = nullptr;
+    size_t scratch_bytes = 0;
+    size_t s_n = 0, s_h = 0, s_dgu = 0, s_dn = 0, s_dxa = 0, s_dxb = 0, s_part = 0, s_dz = 0;
+    float* grads = nullptr;
+    size_t grad_bytes = 0;
+    std::vector<size_t> goff;         // [(chunk*L + block)*4 + which] element offsets
+
+    // kernel timing
+    std::vector<hipEvent_t> ev;
+    std::vector<int> ev_kernel;
+    std::vector<double> ev_flops, ev_bytes;
+    int ev_used = 0;
+    double kt_ms[PPS_K_COUNT] = {};
+    double kt_flops[PPS_K_COUNT] = {};
+    double kt_bytes[PPS_K_COUNT] = {};
+    int64_t kt_n[PPS_K_COUNT] = {};
+};
+
+namespace {
+
+int64_t T_(const pps_stage* h) { return h->d.T; }
+
+char* slot_base(pps_stage* h, int s) { return h->pool + (size_t)s * h->lay.slot_bytes; }
+
+template <typename F>
+hipError_t timed(pps_stage* h, int kernel, double flops, double bytes, F&& launch) {
+    const bool rec = h->profile && h->ev_used < (int)h->ev_kernel.size();
+    if (rec) {
+        hipError_t e = hipEventRecord(h->ev[2 * h->ev_used], h->stream);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = launch();
+    if (e != hipSuccess) return e;
+    if (rec) {
+        e = hipEventRecord(h->ev[2 * h->ev_used + 1], h->stream);
+        if (e != hipSuccess) return e;
+        h->ev_kernel[h->ev_used] = kernel;
+        h->ev_flops[h->ev_used] = flops;
+        h->ev_bytes[h->ev_used] = bytes;
+        ++h->ev_used;
+    }
+    return hipSuccess;
+}
+
+#define PPS_TRY(expr)                          \
+    do {                                       \
+        hipError_t _e = (expr);                \
+        if (_e != hipSuccess) {                \
+            h->failed = true;                  \
+            return PPS_EHIP;                   \
+        }                                      \
+    } while (0)
+
+Layout make_layout(const pps_stage_desc& d, bool swiglu, bool split, int es) {
+    Layout L;
+    const size_t T = (size_t)d.T, dm = (size_t)d.d, f = (size_t)d.ffn;
+    size_t off = 0;
+    const int nb = d.L;
+    auto take = [&](std::vector<size_t>& v, size_t bytes) { v.push_back(off); off += align256(bytes); };
+    for (int b = 0; b < nb; ++b) {
+        if (swiglu) {
+            take(L.x, T * dm * es);
+            take(L.r, T * 4);
+            take(L.g, T * f * es);
+            take(L.u, T * f * es);
+        } else {
+            take(L.x, T * dm * 4);
+            take(L.z, T * dm * 4);
+        }
+    }
+    L.fwd_bytes = off;
+    if (split) {
+        for (int b = 0; b < nb; ++b) {
+            if (swiglu) {
+                take(L.dgu, T * 2 * f * es);
+                take(L.dy, T * dm * es);
+            } else {
+                take(L.dz, T * dm * 4);
+            }
+        }
+    }
+    L.split_bytes = off - L.fwd_bytes;
+    L.slot_bytes = std::max<size_t>(off, 256);
+    return L;
+}
+
+int validate_desc(const pps_stage_desc* d) {
+    if (!d) return PPS_EINVAL;
+    if (d->block_type != PPS_BLOCK_SWIGLU && d->block_type != PPS_BLOCK_TOY_GELU) return PPS_EINVAL;
+    if (d->dtype != PPS_DTYPE_BF16 && d->dtype != PPS_DTYPE_FP32) return PPS_EINVAL;
+    if (d->block_type == PPS_BLOCK_TOY_GELU && d->dtype != PPS_DTYPE_FP32) return PPS_EINVAL;
+    if (d->L < 1 || d->d < 8 || d->d % 8 != 0 || d->d > 16384 || d->T < 0) return PPS_EINVAL;
+    if (d->block_type == PPS_BLOCK_SWIGLU && (d->ffn < 8 || d->ffn % 8 != 0)) return PPS_EINVAL;
+    if (!(d->eps >= 0.0f)) return PPS_EINVAL;
+    if ((d->flags & PPS_FLAG_PROFILE) && d->profile_capacity < 0) return PPS_EINVAL;
+    if (!(d->flags & PPS_FLAG_BOOKKEEPING_ONLY)) {
+        if (!d->weights) return PPS_EINVAL;
+        const int nw = d->block_type == PPS_BLOCK_SWIGLU ? 4 : 2;
+        for (int i = 0; i < d->v * d->L * nw; ++i)
+            if (!d->weights[i]) return PPS_EINVAL;
+    }
+    return PPS_OK;
+}
+
+void release(pps_stage* h) {
+    if (!h) return;
+    for (hipEvent_t e : h->ev)
+        if (e) hipEventDestroy(e);
+    if (h->pool) hipFree(h->pool);
+    if (h->scratch) hipFree(h->scratch);
+    if (h->grads) hipFree(h->grads);
+    delete h;
+}
+
+void maybe_new_pass(pps_stage* h) {
+    if (h->fpos == h->fseq.size() && h->bpos == h->bseq.size() && h->wpos == h->wseq.size()) {
+        h->fpos = h->bpos = h->wpos = 0;
+        std::fill(h->status.begin(), h->status.end(), ST_NONE);
+        h->oplog.clear();
+        ++h->st.passes_completed;
+    }
+}
+
+void log_op(pps_stage* h, int op, int mb, int chunk, int slot, int t) {
+    pps_op rec;
+    rec.op = op;
+    rec.mb = mb;
+    rec.chunk = chunk;
+    rec.slot = slot;
+    rec.inflight_after = h->live;
+    rec.t_start = t;
+    h->oplog.push_back(rec);
+    h->st.live_entries = h->live;
+    h->st.live_bytes = h->live_bytes;
+    h->st.peak_live_entries = std::max<int64_t>(h->st.peak_live_entries, h->live);
+    h->st.peak_live_bytes = std::max<int64_t>(h->st.peak_live_bytes, h->live_bytes);
+}
+
+double gemm_flops(double M, double N, double K) { return 2.0 * M * N * K; }
+
+// ---- SwiGLU block sequences ------------------------------------------------
+
+int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_out) {
+    const pps_stage_desc& D = h->d;
+    const int64_t T = D.T, d = D.d, f = D.ffn;
+    const int dt = D.dtype, es = h->es;
+    char* sb = slot_base(h, slot);
+    char* sn = h->scratch + h->s_n;
+    char* sh = h->scratch + h->s_h;
+    for (int b = 0; b < D.L; ++b) {
+        const void* const* wb = h->w.data() + (size_t)(chunk * D.L + b) * 4;
+        const float* gamma = static_cast<const float*>(wb[3]);
+        char* xb = sb + h->lay.x[b];
+        float* rb = reinterpret_cast<float*>(sb + h->lay.r[b]);
+        char* gb = sb + h->lay.g[b];
+        char* ub = sb + h->lay.u[b];
+        const void* xin = b == 0 ? x_in : xb;
+        // r and n = x r gamma ([T,d]); block 0 also copies x into the stash.
+        PPS_TRY(timed(h, PPS_K_RMSNORM_FWD, 0.0, (double)T * d * es * (b == 0 ? 3 : 2) + T * 4.0 + d * 4.0, [&] {
+            return pps::rmsnorm_fwd(dt, xin, gamma, D.eps, T, d, rb, sn, b == 0 ? xb : nullptr, h->stream);
+        }));
+        // g, u = n [Wg | Wu] with h = silu(g) u in the epilogue.
+        GemmArgs a;
+        a.M = T; a.N = f; a.nseg = 1;
+        a.seg[0].A = sn; a.seg[0].lda = d; a.seg[0].K = d;
+        a.seg[0].B = wb[0]; a.seg[0].B2 = wb[1]; a.seg[0].ldb = f;
+        a.a_kcontig = true; a.b_kcontig = false; a.swiglu_map = true;
+        a.epi = pps::EPI_SWIGLU;
+        a.e.out0 = gb; a.e.out1 = ub; a.e.out2 = sh; a.e.ld0 = f;
+        PPS_TRY(timed(h, PPS_K_GATEUP, gemm_flops(T, 2.0 * f, d), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
+        // y = x + h Wd, written as the next block's x (or the stage output).
+        GemmArgs c;
+        c.M = T; c.N = d; c.nseg = 1;
+        c.seg[0].A = sh; c.seg[0].lda = f; c.seg[0].K = f;
+        c.seg[0].B = wb[2]; c.seg[0].ldb = d;
+        c.a_kcontig = true; c.b_kcontig = false;
+        c.epi = pps::EPI_RESID;
+        c.e.out0 = b == D.L - 1 ? y_out : static_cast<void*>(sb + h->lay.x[b + 1]);
+        c.e.ld0 = d; c.e.in0 = xb; c.e.ldi0 = d;
+        PPS_TRY(timed(h, PPS_K_DOWN, gemm_flops(T, d, f), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
+    }
+    return PPS_OK;
+}
+
+// Weight gradient of block b: dWd += h^T dy; dWg += n^T dg; dWu += n^T du,
+// with n and h recomputed from the stash.
+int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, const void* dgu) {
+    const pps_stage_desc& D = h->d;
+    const int64_t T = D.T, d = D.d, f = D.ffn;
+    const int dt = D.dtype, es = h->es;
+    char* sb = slot_base(h, slot);
+    char* sn = h->scratch + h->s_n;
+    char* sh = h->scratch + h->s_h;
+    const void* const* wb = h->w.data() + (size_t)(chunk * D.L + b) * 4;
+    const float* gamma = static_cast<const float*>(wb[3]);
+    const size_t gi = (size_t)(chunk * D.L + b) * 4;
+    float* dWg = h->grads + h->goff[gi + 0];
+    float* dWu = h->grads + h->goff[gi + 1];
+    float* dWd = h->grads + h->goff[gi + 2];
+    PPS_TRY(timed(h, PPS_K_PREP_W, 0.0, (double)T * (2.0 * d + 3.0 * f) * es + T * 4.0 + d * 4.0, [&] {
+        return pps::prep_w(dt, sb + h->lay.x[b], reinterpret_cast<const float*>(sb + h->lay.r[b]), gamma,
+                           sb + h->lay.g[b], sb + h->lay.u[b], T, d, f, sn, sh, h->stream);
+    }));
+    GemmArgs a;
+    a.M = f; a.N = d; a.nseg = 1;
+    a.seg[0].A = sh; a.seg[0].lda = f; a.seg[0].K = T;
+    a.seg[0].B = dy; a.seg[0].ldb = d;
+    a.a_kcontig = false; a.b_kcontig = false;
+    a.epi = pps::EPI_ACC_F32;
+    a.e.out0 = dWd; a.e.ld0 = d; a.e.nsplit = d;
+    PPS_TRY(timed(h, PPS_K_WGRAD_DOWN, gemm_flops(f, d, T), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
+    GemmArgs c;
+    c.M = d; c.N = 2 * f; c.nseg = 1;
+    c.seg[0].A = sn; c.seg[0].lda = d; c.seg[0].K = T;
+    c.seg[0].B = dgu; c.seg[0].ldb = 2 * f;
+    c.a_kcontig = false; c.b_kcontig = false;
+    c.epi = pps::EPI_ACC_F32;
+    c.e.out0 = dWg; c.e.ld0 = f; c.e.out1 = dWu; c.e.ld1 = f; c.e.nsplit = f;
+    PPS_TRY(timed(h, PPS_K_WGRAD_GATEUP, gemm_flops(d, 2.0 * f, T), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
+    return PPS_OK;
+}
+
+int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* dx_out) {
+    const pps_stage_desc& D = h->d;
+    const int64_t T = D.T, d = D.d, f = D.ffn;
+    const int dt = D.dtype, es = h->es;
+    char* sb = slot_base(h, slot);
+    char* dxbuf[2] = {h->scratch + h->s_dxa, h->scratch + h->s_dxb};
+    float* dn = reinterpret_cast<float*>(h->scratch + h->s_dn);
+    float* part = reinterpret_cast<float*>(h->scratch + h->s_part);
+    if (h->split) {
+        // Keep this micro-batch's output gradient for the deferred W.
+        char* dst = sb + h->lay.dy[D.L - 1];
+        PPS_TRY(timed(h, PPS_K_COPY, 0.0, 2.0 * T * d * es, [&] { return pps::copy_bytes(dst, dy_in, T * d * es, h->stream); }));
+    }
+    for (int b = D.L - 1; b >= 0; --b) {
+        const void* const* wb = h->w.data() + (size_t)(chunk * D.L + b) * 4;
+        const float* gamma = static_cast<const float*>(wb[3]);
+        const size_t gi = (size_t)(chunk * D.L + b) * 4;
+        float* dgam = h->grads + h->goff[gi + 3];
+        const void* dy;
+        void* dx;
+        char* dgu;
+        if (h->split) {
+            dy = sb + h->lay.dy[b];
+            dx = b == 0 ? dx_out : static_cast<void*>(sb + h->lay.dy[b - 1]);
+            dgu = sb + h->lay.dgu[b];
+        } else {
+            dy = b == D.L - 1 ? dy_in : static_cast<const void*>(dxbuf[(b + 1) & 1]);
+            dx = b == 0 ? dx_out : static_cast<void*>(dxbuf[b & 1]);
+            dgu = h->scratch + h->s_dgu;
+        }
+        // dh = dy Wd^T, then dg, du from the stashed g, u.
+        GemmArgs a;
+        a.M = T; a.N = f; a.nseg = 1;
+        a.seg[0].A = dy; a.seg[0].lda = d; a.seg[0].K = d;
+        a.seg[0].B = wb[2]; a.seg[0].ldb = d;
+        a.a_kcontig = true; a.b_kcontig = true;
+        a.epi = pps::EPI_SWIGLU_BWD;
+        a.e.in0 = sb + h->lay.g[b]; a.e.in1 = sb + h->lay.u[b]; a.e.ldi0 = f;
+        a.e.out0 = dgu; a.e.ld0 = 2 * f; a.e.nsplit = f;
+        PPS_TRY(timed(h, PPS_K_DH, gemm_flops(T, f, d), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
+        // dn = dg Wg^T + du Wu^T (one accumulator, K = 2 ffn).
+        GemmArgs c;
+        c.M = T; c.N = d; c.nseg = 2;
+        c.seg[0].A = dgu; c.seg[0].lda = 2 * f; c.seg[0].K = f; c.seg[0].B = wb[0]; c.seg[0].ldb = f;
+        c.seg[1].A = dgu + f * es; c.seg[1].lda = 2 * f; c.seg[1].K = f; c.seg[1].B = wb[1]; c.seg[1].ldb = f;
+        c.a_kcontig = true; c.b_kcontig = true;
+        c.epi = pps::EPI_STORE_F32;
+        c.e.out0 = dn; c.e.ld0 = d;
+        PPS_TRY(timed(h, PPS_K_DN, gemm_flops(T, d, 2.0 * f), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
+        // RMSNorm backward + residual, dgamma partials, then their fixed-order sum.
+        int nrows = 0;
+        PPS_TRY(timed(h, PPS_K_RMSNORM_BWD, 0.0,
+                      (double)T * d * 4 + 3.0 * T * d * es + T * 4.0 + d * 4.0 + (double)pps::rmsnorm_bwd_partial_rows(T) * d * 4, [&] {
+                          return pps::rmsnorm_bwd(dt, dn, sb + h->lay.x[b], reinterpret_cast<const float*>(sb + h->lay.r[b]),
+                                                  gamma, dy, T, d, dx, part, &nrows, h->stream);
+                      }));
+        const int prow = pps::rmsnorm_bwd_partial_rows(T);
+        PPS_TRY(timed(h, PPS_K_DGAMMA, 0.0, (double)prow * d * 4 + 8.0 * d, [&] {
+            return pps::column_reduce_acc(part, T > 0 ? prow : 0, d, dgam, h->stream);
+        }));
+        if (!h->split) {
+            int rc = swiglu_weight(h, slot, chunk, b, dy, dgu);
+            if (rc != PPS_OK) return rc;
+        }
+    }
+    return PPS_OK;
+}
+
+int swiglu_backward_weight(pps_stage* h, int slot, int chunk) {
+    char* sb = slot_base(h, slot);
+    for (int b = h->d.L - 1; b >= 0; --b) {
+        int rc = swiglu_weight(h, slot, chunk, b, sb + h->lay.dy[b], sb + h->lay.dgu[b]);
+        if (rc != PPS_OK) return rc;
+    }
+    return PPS_OK;
+}
+
+// ---- toy block sequences (fp32) ---------------------------------------------
+
+int toy_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_out) {
+    const pps_stage_desc& D = h->d;
+    const int64_t T = D.T, d = D.d;
+    char* sb = slot_base(h, slot);
+    PPS_TRY(timed(h, PPS_K_COPY, 0.0, 2.0 * T * d * 4, [&] { return pps::copy_bytes(sb + h->lay.x[0], x_in, T * d * 4, h->stream); }));
+    for (int b = 0; b < D.L; ++b) {
+        const void* const* wb = h->w.data() + (size_t)(chunk * D.L + b) * 2;
+        GemmArgs a;
+        a.M = T; a.N = d; a.nseg = 1;
+        a.seg[0].A = sb + h->lay.x[b]; a.seg[0].lda = d; a.seg[0].K = d;
+        a.seg[0].B = wb[0]; a.seg[0].ldb = d;
+        a.a_kcontig = true; a.b_kcontig = false;
+        a.epi = pps::EPI_BIAS_GELU;
+        a.e.bias = static_cast<const float*>(wb[1]);
+        a.e.out0 = sb + h->lay.z[b]; a.e.ld0 = d;
+        a.e.out1 = b == D.L - 1 ? y_out : static_cast<void*>(sb + h->lay.x[b + 1]); a.e.ld1 = d;
+        PPS_TRY(timed(h, PPS_K_TOY_FWD, gemm_flops(T, d, d), 0.0, [&] { return pps::gemm(PPS_DTYPE_FP32, a, h->stream); }));
+    }
+    return PPS_OK;
+}
+
+int toy_weight(pps_stage* h, int slot, int chunk, int b, const float* dz) {
+    const pps_stage_desc& D = h->d;
+    const int64_t T = D.T, d = D.d;
+    char* sb = slot_base(h, slot);
+    const size_t gi = (size_t)(chunk * D.L + b) * 4;
+    GemmArgs a;
+    a.M = d; a.N = d; a.nseg = 1;
+    a.seg[0].A = sb + h->lay.x[b]; a.seg[0].lda = d; a.seg[0].K = T;
+    a.seg[0].B = dz; a.seg[0].ldb = d;
+    a.a_kcontig = false; a.b_kcontig = false;
+    a.epi = pps::EPI_ACC_F32;
+    a.e.out0 = h->grads + h->goff[gi + 0]; a.e.ld0 = d; a.e.nsplit = d;
+    PPS_TRY(timed(h, PPS_K_TOY_DW, gemm_flops(d, d, T), 0.0, [&] { return pps::gemm(PPS_DTYPE_FP32, a, h->stream); }));
+    PPS_TRY(timed(h, PPS_K_TOY_DB, 0.0, (double)T * d * 4 + 8.0 * d, [&] {
+        return pps::colsum_acc(dz, T, d, h->grads + h->goff[gi + 1], h->stream);
+    }));
+    return PPS_OK;
+}
+
+int toy_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* dx_out) {
+    const pps_stage_desc& D = h->d;
+    const int64_t T = D.T, d = D.d;
+    char* sb = slot_base(h, slot);
+    char* dxbuf[2] = {h->scratch + h->s_dxa, h->scratch + h->s_dxb};
+    for (int b = D.L - 1; b >= 0; --b) {
+        const void* const* wb = h->w.data() + (size_t)(chunk * D.L + b) * 2;
+        const float* dy = static_cast<const float*>(b == D.L - 1 ? dy_in : static_cast<const void*>(dxbuf[(b + 1) & 1]));
+        void* dx = b == 0 ? dx_out : static_cast<void*>(dxbuf[b & 1]);
+        float* dz = reinterpret_cast<float*>(h->split ? sb + h->lay.dz[b] : h->scratch + h->s_dz);
+        PPS_TRY(timed(h, PPS_K_TOY_DZ, 0.0, 3.0 * T * d * 4, [&] {
+            return pps::gelu_bwd(dy, reinterpret_cast<const float*>(sb + h->lay.z[b]), T * d, dz, h->stream);
+        }));
+        GemmArgs a;
+        a.M = T; a.N = d; a.nseg = 1;
+        a.seg[0].A = dz; a.seg[0].lda = d; a.seg[0].K = d;
+        a.seg[0].B = wb[0]; a.seg[0].ldb = d;
+        a.a_kcontig = true; a.b_kcontig = true;
+        a.epi = pps::EPI_STORE;
+        a.e.out0 = dx; a.e.ld0 = d;
+        PPS_TRY(timed(h, PPS_K_TOY_DX, gemm_flops(T, d, d), 0.0, [&] { return pps::gemm(PPS_DTYPE_FP32, a, h->stream); }));
+        if (!h->split) {
+            int rc = toy_weight(h, slot, chunk, b, dz);
+            if (rc != PPS_OK) return rc;
+        }
+    }
+    return PPS_OK;
+}
+
+int toy_backward_weight(pps_stage* h, int slot, int chunk) {
+    char* sb = slot_base(h, slot);
+    for (int b = h->d.L - 1; b >= 0; --b) {
+        int rc = toy_weight(h, slot, chunk, b, reinterpret_cast<const float*>(sb + h->lay.dz[b]));
+        if (rc != PPS_OK) return rc;
+    }
+    return PPS_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+extern "C" int pps_stage_create(const pps_stage_desc* desc, pps_stage** out) {
+    if (!out) return PPS_EINVAL;
+    int rc = validate_desc(desc);
+    if (rc != PPS_OK) return rc;
+    pps_stage* h = new (std::nothrow) pps_stage();
+    if (!h) return PPS_ENOMEM;
+    h->d = *desc;
+    h->bookkeeping = (desc->flags & PPS_FLAG_BOOKKEEPING_ONLY) != 0;
+    h->profile = !h->bookkeeping && (desc->flags & PPS_FLAG_PROFILE) != 0;
+    h->swiglu = desc->block_type == PPS_BLOCK_SWIGLU;
+    h->nw = h->swiglu ? 4 : 2;
+    h->es = desc->dtype == PPS_DTYPE_BF16 ? 2 : 4;
+    h->split = desc->kind == PPS_ZB1P || desc->kind == PPS_ZB2P;
+    h->stream = static_cast<hipStream_t>(desc->stream);
+    h->d.weights = nullptr;
+    if (!h->bookkeeping) h->w.assign(desc->weights, desc->weights + (size_t)desc->v * desc->L * h->nw);
+
+    rc = pps::build_schedule(desc->P, desc->M, desc->k, desc->v, desc->kind, h->sched);
+    if (rc != PPS_OK) { release(h); return rc; }
+    int peak = 0;
+    for (const pps_op& o : h->sched) {
+        peak = std::max(peak, o.inflight_after);
+        if (o.op == PPS_OP_F) { h->fseq.push_back({o.mb, o.chunk}); h->tf.push_back(o.t_start); }
+        else if (o.op == PPS_OP_B) { h->bseq.push_back({o.mb, o.chunk}); h->tb.push_back(o.t_start); }
+        else { h->wseq.push_back({o.mb, o.chunk}); h->tw.push_back(o.t_start); }
+    }
+    h->S = peak;
+    h->status.assign((size_t)desc->M * desc->v, ST_NONE);
+    h->slot_of.assign((size_t)desc->M * desc->v, -1);
+    h->slot_used.assign(h->S, 0);
+
+    h->lay = make_layout(*desc, h->swiglu, h->split, h->es);
+    const size_t T = (size_t)desc->T, dm = (size_t)desc->d, f = (size_t)desc->ffn;
+    size_t off = 0;
+    auto take = [&](size_t& o, size_t bytes) { o = off; off += align256(bytes); };
+    if (h->swiglu) {
+        take(h->s_n, T * dm * h->es);
+        take(h->s_h, T * f * h->es);
+        take(h->s_dgu, h->split ? 256 : T * 2 * f * h->es);
+        take(h->s_dn, T * dm * 4);
+        take(h->s_part, (size_t)pps::rmsnorm_bwd_partial_rows((int64_t)T) * dm * 4);
+    } else {
+        take(h->s_dz, T * dm * 4);
+    }
+    take(h->s_dxa, T * dm * h->es);
+    take(h->s_dxb, T * dm * h->es);
+    h->scratch_bytes = std::max<size_t>(off, 256);
+
+    const int nblk = desc->v * desc->L;
+    size_t goff = 0;
+    for (int i = 0; i < nblk; ++i) {
+        if (h->swiglu) {
+            h->goff.push_back(goff); goff += dm * f;
+            h->goff.push_back(goff); goff += dm * f;
+            h->goff.push_back(goff); goff += f * dm;
+            h->goff.push_back(goff); goff += dm;
+        } else {
+            h->goff.push_back(goff); goff += dm * dm;
+            h->goff.push_back(goff); goff += dm;
+            h->goff.push_back(goff);
+            h->goff.push_back(goff);
+        }
+        goff = (goff + 63) & ~size_t(63);
+    }
+    h->grad_bytes = goff * sizeof(float);
+
+    h->st.n_slots = h->S;
+    h->st.slot_bytes = (int64_t)h->lay.slot_bytes;
+    h->st.pool_bytes = (int64_t)h->lay.slot_bytes * h->S;
+    h->st.scratch_bytes = (int64_t)h->scratch_bytes;
+    h->st.grad_bytes = (int64_t)h->grad_bytes;
+
+    if (!h->bookkeeping) {
+        if (hipMalloc(reinterpret_cast<void**>(&h->pool), std::max<size_t>(h->lay.slot_bytes * h->S, 256)) != hipSuccess ||
+            hipMalloc(reinterpret_cast<void**>(&h->scratch), h->scratch_bytes) != hipSuccess ||
+            hipMalloc(reinterpret_cast<void**>(&h->grads), std::max<size_t>(h->grad_bytes, 256)) != hipSuccess) {
+            (void)hipGetLastError();
+            release(h);
+            return PPS_ENOMEM;
+        }
+        if (pps::fill_zero(h->grads, (int64_t)h->grad_bytes, h->stream) != hipSuccess) { release(h); return PPS_EHIP; }
+        if (h->profile) {
+            const int cap = desc->profile_capacity;
+            h->ev.assign((size_t)cap * 2, nullptr);
+            h->ev_kernel.assign(cap, 0);
+            h->ev_flops.assign(cap, 0.0);
+            h->ev_bytes.assign(cap, 0.0);
+            for (auto& e : h->ev)
+                if (hipEventCreate(&e) != hipSuccess) { release(h); return PPS_EHIP; }
+        }
+        if (hipStreamSynchronize(h->stream) != hipSuccess) { release(h); return PPS_EHIP; }
+    }
+    *out = h;
+    return PPS_OK;
+}
+
+extern "C" int pps_stage_forward(pps_stage* h, int mb, int chunk, const void* x_in, void* y_out) {
+    if (!h) return PPS_EINVAL;
+    if (h->failed) return PPS_EHIP;
+    if (mb < 0 || mb >= h->d.M || chunk < 0 || chunk >= h->d.v) return PPS_EINVAL;
+    if (!h->bookkeeping && (!x_in || !y_out)) return PPS_EINVAL;
+    maybe_new_pass(h);
+    if (h->fpos >= h->fseq.size() || h->fseq[h->fpos] != std::make_pair(mb, chunk)) return PPS_EORDER;
+    int slot = 0;
+    while (slot < h->S && h->slot_used[slot]) ++slot;
+    if (slot == h->S) return PPS_EFULL;
+
+    if (!h->bookkeeping) {
+        int rc = h->swiglu ? swiglu_forward(h, slot, chunk, x_in, y_out) : toy_forward(h, slot, chunk, x_in, y_out);
+        if (rc != PPS_OK) return rc;
+    }
+    const size_t key = (size_t)chunk * h->d.M + mb;
+    h->slot_used[slot] = 1;
+    h->slot_of[key] = slot;
+    h->status[key] = ST_F;
+    ++h->live;
+    h->live_bytes += (int64_t)h->lay.fwd_bytes;
+    log_op(h, PPS_OP_F, mb, chunk, slot, h->tf[h->fpos]);
+    ++h->fpos;
+    ++h->st.n_forward;
+    return PPS_OK;
+}
+
+extern "C" int pps_stage_backward(pps_stage* h, int mb, int chunk, const void* dy_in, void* dx_out) {
+    if (!h) return PPS_EINVAL;
+    if (h->failed) return PPS_EHIP;
+    if (mb < 0 || mb >= h->d.M || chunk < 0 || chunk >= h->d.v) return PPS_EINVAL;
+    if (!h->bookkeeping && (!dy_in || !dx_out)) return PPS_EINVAL;
+    const size_t key = (size_t)chunk * h->d.M + mb;
+    if (h->status[key] == ST_NONE) return PPS_ENOENT;
+    if (h->status[key] != ST_F) return PPS_ESTATE;
+    if (h->bpos >= h->bseq.size() || h->bseq[h->bpos] != std::make_pair(mb, chunk)) return PPS_EORDER;
+    const int slot = h->slot_of[key];
+
+    if (!h->bookkeeping) {
+        int rc = h->swiglu ? swiglu_backward(h, slot, chunk, dy_in, dx_out) : toy_backward(h, slot, chunk, dy_in, dx_out);
+        if (rc != PPS_OK) return rc;
+    }
+    if (h->split) {
+        h->status[key] = ST_B;
+        h->live_bytes += (int64_t)h->lay.split_bytes;
+    } else {
+        h->status[key] = ST_W;
+        h->slot_used[slot] = 0;
+        --h->live;
+        h->live_bytes -= (int64_t)h->lay.fwd_bytes;
+    }
+    log_op(h, PPS_OP_B, mb, chunk, slot, h->tb[h->bpos]);
+    ++h->bpos;
+    ++h->st.n_backward;
+    return PPS_OK;
+}
+
+extern "C" int pps_stage_backward_weight(pps_stage* h, int mb, int chunk) {
+    if (!h) return PPS_EINVAL;
+    if (h->failed) return PPS_EHIP;
+    if (mb < 0 || mb >= h->d.M || chunk < 0 || chunk >= h->d.v) return PPS_EINVAL;
+    if (!h->split) return PPS_ESTATE;
+    const size_t key = (size_t)chunk * h->d.M + mb;
+    if (h->status[key] != ST_B) return PPS_ESTATE;
+    if (h->wpos >= h->wseq.size() || h->wseq[h->wpos] != std::make_pair(mb, chunk)) return PPS_EORDER;
+    const int slot = h->slot_of[key];
+    if (!h->bookkeeping) {
+        int rc = h->swiglu ? swiglu_backward_weight(h, slot, chunk) : toy_backward_weight(h, slot, chunk);
+        if (rc != PPS_OK) return rc;
+    }
+    h->status[key] = ST_W;
+    h->slot_used[slot] = 0;
+    --h->live;
+    h->live_bytes -= (int64_t)(h->lay.fwd_bytes + h->lay.split_bytes);
+    log_op(h, PPS_OP_W, mb, chunk, slot, h->tw[h->wpos]);
+    ++h->wpos;
+    ++h->st.n_backward_weight;
+    return PPS_OK;
+}
+
+extern "C" int pps_stage_zero_grad(pps_stage* h) {
+    if (!h) return PPS_EINVAL;
+    if (h->failed) return PPS_EHIP;
+    if (h->bookkeeping) return PPS_OK;
+    if (pps::fill_zero(h->grads, (int64_t)h->grad_bytes, h->stream) != hipSuccess) { h->failed = true; return PPS_EHIP; }
+    return PPS_OK;
+}
+
+extern "C" int pps_stage_get_grad(const pps_stage* h, int chunk, int block, int which, const float** dptr) {
+    if (!h || !dptr || h->bookkeeping) return PPS_EINVAL;
+    if (chunk < 0 || chunk >= h->d.v || block < 0 || block >= h->d.L) return PPS_EINVAL;
+    if (which < 0 || which >= (h->swiglu ? 4 : 2)) return PPS_EINVAL;
+    *dptr = h->grads + h->goff[(size_t)(chunk * h->d.L + block) * 4 + which];
+    return PPS_OK;
+}
+
+extern "C" int pps_stage_sync(pps_stage* h) {
+    if (!h) return PPS_EINVAL;
+    if (h->bookkeeping) return PPS_OK;
+    if (hipStreamSynchronize(h->stream) != hipSuccess) { h->failed = true; return PPS_EHIP; }
+    if (hipGetLastError() != hipSuccess) { h->failed = true; return PPS_EHIP; }
+    return h->failed ? PPS_EHIP : PPS_OK;
+}
+
+extern "C" int pps_stage_get_stats(const pps_stage* h, pps_stats* out) {
+    if (!h || !out) return PPS_EINVAL;
+    *out = h->st;
+    out->live_entries = h->live;
+    out->live_bytes = h->live_bytes;
+    return PPS_OK;
+}
+
+extern "C" int pps_stage_get_oplog(const pps_stage* h, pps_op* ops, int cap, int* n) {
+    if (!h || !n || cap < 0 || (cap > 0 && !ops)) return PPS_EINVAL;
+    *n = (int)h->oplog.size();
+    if (cap < *n) return PPS_EFULL;
+    if (*n) std::memcpy(ops, h->oplog.data(), h->oplog.size() * sizeof(pps_op));
+    return PPS_OK;
+}
+
+extern "C" int pps_stage_kernel_times(pps_stage* h, pps_kernel_time* out, int cap, int* n) {
+    if (!h || !n || !h->profile || cap < 0 || (cap > 0 && !out)) return PPS_EINVAL;
+    if (hipStreamSynchronize(h->stream) != hipSuccess) { h->failed = true; return PPS_EHIP; }
+    for (int i = 0; i < h->ev_used; ++i) {
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, h->ev[2 * i], h->ev[2 * i + 1]) != hipSuccess) { h->failed = true; return PPS_EHIP; }
+        const int k = h->ev_kernel[i];
+        h->kt_ms[k] += ms;
+        h->kt_flops[k] += h->ev_flops[i];
+        h->kt_bytes[k] += h->ev_bytes[i];
+        ++h->kt_n[k];
+    }
+    h->ev_used = 0;
+    int cnt = 0;
+    for (int k = 0; k < PPS_K_COUNT; ++k)
+        if (h->kt_n[k]) ++cnt;
+    *n = cnt;
+    if (cap < cnt) return PPS_EFULL;
+    int j = 0;
+    for (int k = 0; k < PPS_K_COUNT; ++k) {
+        if (!h->kt_n[k]) continue;
+        out[j].kernel = k;
+        out[j].reserved = 0;
+        out[j].launches = h->kt_n[k];
+        out[j].total_ms = h->kt_ms[k];
+        out[j].flops = h->kt_flops[k];
+        out[j].bytes = h->kt_bytes[k];
+        ++j;
+        h->kt_n[k] = 0;
+        h->kt_ms[k] = h->kt_flops[k] = h->kt_bytes[k] = 0.0;
+    }
+    return PPS_OK;
+}
+
+extern "C" const char* pps_kernel_name(int k) {
+    static const char* names[PPS_K_COUNT] = {
+        "rmsnorm_fwd", "gemm_gateup_swiglu", "gemm_down_residual", "gemm_dh_swiglu_bwd", "gemm_dn",
+        "rmsnorm_bwd_residual", "dgamma_reduce", "prep_w", "gemm_wgrad_down", "gemm_wgrad_gateup",
+        "copy", "toy_fwd", "toy_dz", "toy_dx", "toy_dw", "toy_db"};
+    return (k >= 0 && k < PPS_K_COUNT) ? names[k] : "unknown";
+}
+
+extern "C" int pps_scale(void* dst, const void* src, int64_t n, float sc, int dtype, void* stream) {
+    if (n < 0 || (n > 0 && (!dst || !src))) return PPS_EINVAL;
+    if (dtype != PPS_DTYPE_BF16 && dtype != PPS_DTYPE_FP32) return PPS_EINVAL;
+    return pps::scale(dtype, dst, src, n, sc, static_cast<hipStream_t>(stream)) == hipSuccess ? PPS_OK : PPS_EHIP;
+}
+
+extern "C" void pps_stage_destroy(pps_stage* h) {
+    if (!h) return;
+    if (!h->bookkeeping) (void)hipStreamSynchronize(h->stream);
+    release(h);
+}
+
+extern "C" const char* pps_strerror(int s) {
+    switch (s) {
+        case PPS_OK: return "ok";
+        case PPS_EINVAL: return "invalid argument";
+        case PPS_EFULL: return "no room (op array too small or no free stash slot)";
+        case PPS_EORDER: return "call is not the next one of its kind in the schedule";
+        case PPS_ENOENT: return "no saved forward for this micro-batch";
+        case PPS_ESTATE: return "wrong state for this call";
+        case PPS_ENOMEM: return "device allocation failed";
+        case PPS_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}

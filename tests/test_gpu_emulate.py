@@ -1,0 +1,71 @@
+"""P-stage emulation on one GPU against the oracle's whole-model step
+(linear-probe loss, dy = G / M at the last stage)."""
+
+import pytest
+
+from oracle import numerics as N
+
+pytestmark = pytest.mark.gpu
+
+
+def _emulate(cfg, kind="1f1b", gamma=None, bias=None):
+    import torch
+    from pipeline_schedules_amd import pps
+    from pipeline_schedules_amd.emulate import run_pipeline
+    from pipeline_schedules_amd.inputs import make_inputs
+    from tests import gpu_util as G
+
+    inp = make_inputs(cfg, stages=range(cfg.P), gamma=gamma, bias=bias)
+    stream = torch.cuda.current_stream()
+    stages = []
+    for k in range(cfg.P):
+        w = G.upload_params(inp.params[k], cfg.block, cfg.dtype)
+        stages.append(pps.stage_from_config(cfg, weights=w, k=k, kind=kind, stream=stream))
+    xs = [G.to_dev(x, cfg.dtype) for x in inp.xs]
+    Gs = [G.to_dev(g, cfg.dtype) for g in inp.Gs]
+    ys, dxs = run_pipeline(stages, xs, Gs, pps.DTYPE_BY_NAME[cfg.dtype], pps.KIND_BY_NAME[kind])
+    grads = [G.stage_grads(st, cfg.L, cfg.block, cfg.d, cfg.f) for st in stages]
+    for k, st in enumerate(stages):
+        s = st.stats()
+        sched = pps.make_schedule(cfg.P, cfg.M, k, 1, pps.KIND_BY_NAME[kind])
+        assert s["peak_live_entries"] == max(o[4] for o in sched)
+        if kind != "zb1p":
+            assert s["peak_live_entries"] == (cfg.M if kind == "gpipe" else min(cfg.P - k, cfg.M))
+        st.close()
+    rys, rdxs, rgrads = N.pipeline_model_step(inp.xs, inp.Gs, inp.params, cfg.block, cfg.eps)
+    errs = {}
+    for i in range(cfg.M):
+        errs[f"y{i}"] = N.rel_l2(G.to_host(ys[i]), rys[i])
+        errs[f"dx{i}"] = N.rel_l2(G.to_host(dxs[i]), rdxs[i])
+    for k in range(cfg.P):
+        for b in range(cfg.L):
+            for key in rgrads[k][b]:
+                errs[f"s{k}b{b}{key}"] = N.rel_l2(grads[k][b][key], rgrads[k][b][key])
+    return errs
+
+
+@pytest.mark.parametrize("kind", ["1f1b", "gpipe", "zb1p"])
+def test_emulation_toy_two_stages(kind):
+    # 2 stages x 4 micro-batches, each stage 2 x (Linear 64->64 + GELU), fp32.
+    from pipeline_schedules_amd.configs import C1_TOY
+    errs = _emulate(C1_TOY, kind, bias="random")
+    bad = {k: v for k, v in errs.items() if not v <= 1e-5}
+    assert not bad, bad
+
+
+def test_emulation_swiglu_four_stages():
+    # 4 stages x 6 micro-batches, 2 SwiGLU blocks per stage, d=1024, ffn=2816,
+    # micro-batch 4x512 tokens, bf16.
+    from pipeline_schedules_amd.configs import C2_SMALL
+    errs = _emulate(C2_SMALL, "1f1b")
+    print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= 2e-2}
+    assert not bad, bad
+
+
+def test_emulation_swiglu_zb1p_small():
+    from pipeline_schedules_amd.configs import C2_SMALL
+    cfg = C2_SMALL.with_(P=4, M=8, d=256, f=512, T=264, L=1, kind="zb1p")
+    errs = _emulate(cfg, "zb1p", gamma="random")
+    bad = {k: v for k, v in errs.items() if not v <= 2e-2}
+    assert not bad, bad
