@@ -1,0 +1,231 @@
+"""Benchmark: one pipeline stage's F+B throughput on one MI355X.
+
+Workload (default): stage k=0 of an 8-stage, 16-micro-batch 1F1B pipeline of
+an 80-layer model -- 10 residual SwiGLU blocks, d=8192, ffn=28672, micro-batch
+2x4096 = 8192 tokens, bf16 -- i.e. the stage's 32-op list F0..F7, then
+(B_j, F_{8+j}) pairs, then B8..B15.  One step = one full pass of that op list
+over 16 micro-batches with the inputs resident in HBM.  Inputs are seeded
+synthetic data (weights N(0,0.02), x N(0,1), output gradients N(0,0.01)).
+
+Prints one JSON line: stage F+B TFLOP/s (algorithmic 18*T*d*ffn per block per
+micro-batch), its fraction of the bf16 dense MFMA peak, peak stash bytes, the
+dominant kernel's roofline from HIP events recorded around every launch in
+the timed region, and the float64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, params_dev, budget_s=15.0):
+    """Time the float64 oracle (numpy/OpenBLAS, all host cores it is given) on
+    one SwiGLU block of this workload's width, forward + backward on a sample
+    of tokens sized to take roughly ``budget_s`` seconds."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import numerics as N
+
+    p = params_dev[0]
+    host = {k: p[k].float().cpu().numpy().astype(np.float64) for k in ("Wg", "Wu", "Wd")}
+    host["gamma"] = p["gamma"].float().cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(0)
+
+    def run(ts):
+        x = rng.normal(0, 1, (ts, cfg.d))
+        dy = rng.normal(0, 0.01, (ts, cfg.d))
+        t0 = time.perf_counter()
+        y, s = N.swiglu_forward(x, host, cfg.eps)
+        N.swiglu_backward(s, dy, host)
+        return time.perf_counter() - t0
+
+    ts = 64
+    dt = run(ts)
+    while dt < budget_s / 4 and ts < 4096:
+        ts *= 2
+        dt = run(ts)
+    flops = 18.0 * ts * cfg.d * cfg.f
+    threads = 0
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 0)))
+    del host
+    torch.cuda.synchronize()
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads or len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"one SwiGLU block (d={cfg.d}, ffn={cfg.f}) forward+backward on {ts} tokens in float64 "
+                  f"({flops / 1e12:.2f} TFLOP, {dt:.1f} s); weights = block 0 of the benchmark inputs",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="c3_80layer_p8_stage0")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one pipeline stage on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU transport between stages is not part of this build)", file=sys.stderr)
+        sys.exit(1)
+
+    import torch
+
+    from pipeline_schedules_amd import pps
+    from pipeline_schedules_amd.configs import PRESETS
+    from pipeline_schedules_amd.inputs import make_device_inputs
+
+    cfg = PRESETS[args.config]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    dtype_id = pps.DTYPE_BY_NAME[cfg.dtype]
+    kind_id = pps.KIND_BY_NAME[cfg.kind]
+
+    _log(f"workload {cfg.name}: drawing inputs on the device")
+    inp = make_device_inputs(cfg, dev)
+    weights = []
+    for p in inp["params"]:
+        weights += [p["Wg"], p["Wu"], p["Wd"], p["gamma"]] if cfg.block == "swiglu" else [p["W"], p["b"]]
+    ops = pps.make_schedule(cfg.P, cfg.M, cfg.k, cfg.v, kind_id)
+    launches_per_pass = 0
+    per_block_f = 3 if cfg.block == "swiglu" else 2
+    per_block_b = 7 if cfg.block == "swiglu" else 5
+    launches_per_pass = cfg.M * cfg.v * cfg.L * (per_block_f + per_block_b) + 2 * cfg.M * cfg.v
+    flags = 0 if args.no_profile else pps.FLAG_PROFILE
+    st = pps.stage_from_config(cfg, weights=weights, stream=stream, flags=flags,
+                               profile_capacity=launches_per_pass * (args.steps + 1))
+    T, d = cfg.T, cfg.d
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    xs = inp["xs"]
+    if cfg.v > 1:   # later chunks take their own synthetic inputs on one device
+        xs2 = make_device_inputs(cfg.with_(seed=cfg.seed + 1), dev, with_G=True)
+        chunk_x = [xs] + [xs2["xs"]] * (cfg.v - 1)
+        chunk_g = [inp["Gs"]] + [xs2["Gs"]] * (cfg.v - 1)
+    else:
+        chunk_x, chunk_g = [xs], [inp["Gs"]]
+    y = torch.empty((T, d), dtype=tdt, device=dev)
+    dx = torch.empty((T, d), dtype=tdt, device=dev)
+
+    def one_pass():
+        for op, mb, c, *_ in ops:
+            if op == pps.OP_F:
+                st.forward(mb, c, chunk_x[c][mb], y)
+            elif op == pps.OP_B:
+                st.backward(mb, c, chunk_g[c][mb], dx)
+            else:
+                st.backward_weight(mb, c)
+
+    st.zero_grad()
+    _log(f"warmup: {args.warmup} pass(es) of {len(ops)} ops")
+    for _ in range(args.warmup):
+        one_pass()
+    st.sync()
+    if not args.no_profile:
+        st.kernel_times()   # drop warm-up timings
+    torch.cuda.synchronize()
+    _log(f"timed: {args.steps} pass(es)")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        one_pass()
+    e1.record(stream)
+    st.sync()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / args.steps
+    flops_per_pass = cfg.flops_per_microbatch() * cfg.M
+    tflops = flops_per_pass / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    stats = st.stats()
+
+    roofline = None
+    kernels = {}
+    if not args.no_profile:
+        kt = st.kernel_times()
+        for k in kt:
+            kernels[k["name"]] = {
+                "launches": k["launches"], "avg_ms": k["total_ms"] / k["launches"],
+                "total_ms_per_step": k["total_ms"] / args.steps,
+                "tflops": (k["flops"] / (k["total_ms"] * 1e-3) / 1e12) if k["flops"] else None,
+                "gbs": (k["bytes"] / (k["total_ms"] * 1e-3) / 1e9) if k["bytes"] else None,
+            }
+        dom = max(kt, key=lambda k: k["total_ms"])
+        if dom["flops"]:
+            ach = dom["flops"] / (dom["total_ms"] * 1e-3) / 1e12
+            roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(ach / peak, 4), "traffic": None, "kernel": dom["name"],
+                        "avg_launch_ms": dom["total_ms"] / dom["launches"],
+                        "flops_per_launch": dom["flops"] / dom["launches"]}
+        else:
+            ach = dom["bytes"] / (dom["total_ms"] * 1e-3) / 1e9
+            roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom["name"],
+                        "avg_launch_ms": dom["total_ms"] / dom["launches"],
+                        "bytes_per_launch": dom["bytes"] / dom["launches"]}
+
+    cpu = None
+    if not args.no_cpu_baseline and cfg.block == "swiglu":
+        _log("cpu baseline: float64 oracle on a token sample")
+        cpu = cpu_baseline(cfg, inp["params"])
+    st.close()
+
+    out = {
+        "metric": "stage F+B TFLOP/s & MFMA-peak fraction at P=8 slice; peak stash bytes",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: stage k={cfg.k} of P={cfg.P}, M={cfg.M} micro-batches, "
+                               f"{cfg.kind}{' v=' + str(cfg.v) if cfg.v > 1 else ''}, {cfg.L * cfg.v} SwiGLU blocks "
+                               f"d={cfg.d} ffn={cfg.f}, {cfg.T} tokens/micro-batch",
+                   "P": cfg.P, "M": cfg.M, "k": cfg.k, "v": cfg.v, "schedule": cfg.kind, "blocks": cfg.L * cfg.v,
+                   "d": cfg.d, "ffn": cfg.f, "tokens_per_microbatch": cfg.T, "ops_per_step": len(ops)},
+        "peak_fraction": round(tflops / peak, 4),
+        "peak_stash_bytes": stats["peak_live_bytes"],
+        "peak_stash_entries": stats["peak_live_entries"],
+        "stash_bound_entries": max(o[4] for o in ops),
+        "flops_per_step": flops_per_pass,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
