@@ -198,6 +198,61 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ a
     out[j] += s;
 }
 
+// 64 x 64 tile transposes through LDS.  Source rows r < rows, columns
+// c < cols (cols % 8 == 0); destination row map(c), column r, stride ldd
+// (ldd % 8 == 0); destination columns in [rows, ldd) are written as zero.
+// map(c) = c, or with grp > 0: (c / grp) * 2 grp + half * grp + c % grp
+// (gate/up interleave of the forward weight copy).
+//   MODE 0: dst = src
+//   MODE 1: dst = (src * r[row]) * gamma[col]        (RMSNorm output n)
+//   MODE 2: dst = silu(src) * src2                    (SwiGLU output h)
+template <typename S, int MODE>
+__global__ __launch_bounds__(256) void tile_transpose_kernel(const S* __restrict__ src, const S* __restrict__ src2,
+                                                             const float* __restrict__ r, const float* __restrict__ gamma,
+                                                             int64_t rows, int64_t cols, int64_t lds, S* __restrict__ dst,
+                                                             int64_t ldd, int grp, int half) {
+    __shared__ float tile[64][65];
+    const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = t + 256 * i, rr = q >> 3, c8 = (q & 7) * 8;
+        const int64_t row = r0 + rr, col = c0 + c8;
+        float v[8];
+        if (row < rows && col < cols) {
+            Vec8<S>::load(src + row * lds + col, v);
+            if constexpr (MODE == 1) {
+                const float rv = r[row];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = (v[j] * rv) * gamma[col + j];
+            } else if constexpr (MODE == 2) {
+                float u[8];
+                Vec8<S>::load(src2 + row * lds + col, u);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = swiglu_f(v[j], u[j]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tile[rr][c8 + j] = v[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = t + 256 * i, cc = q >> 3, r8 = (q & 7) * 8;
+        const int64_t col = c0 + cc, row = r0 + r8;
+        if (col < cols && row < ldd) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = tile[r8 + j][cc];
+            const int64_t drow = grp ? (col / grp) * 2 * grp + (int64_t)half * grp + col % grp : col;
+            Vec8<S>::store(dst + drow * ldd + row, v);
+        }
+    }
+}
+
 template <typename S>
 __global__ __launch_bounds__(256) void scale_kernel(S* __restrict__ dst, const S* __restrict__ src, int64_t n,
                                                     float sc) {
@@ -302,6 +357,23 @@ hipError_t gelu_bwd(const float* dy, const float* z, int64_t count, float* dz, h
 hipError_t colsum_acc(const float* a, int64_t T, int64_t d, float* out, hipStream_t s) {
     if (T <= 0 || d <= 0) return hipSuccess;
     hipLaunchKernelGGL(colsum_kernel, dim3(grid_for(d)), dim3(256), 0, s, a, T, d, out);
+    return hipGetLastError();
+}
+
+hipError_t transpose(int dtype, int mode, const void* src, const void* src2, const float* r, const float* gamma,
+                     int64_t rows, int64_t cols, int64_t lds, void* dst, int64_t ldd, int grp, int half, hipStream_t s) {
+    if (cols <= 0 || ldd <= 0) return hipSuccess;
+    if (cols % 8 || ldd % 8 || lds % 8) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((ldd + 63) / 64), (unsigned)((cols + 63) / 64));
+#define PPS_TR(S, MODE)                                                                                          \
+    hipLaunchKernelGGL((tile_transpose_kernel<S, MODE>), grid, dim3(256), 0, s, static_cast<const S*>(src),        \
+                       static_cast<const S*>(src2), r, gamma, rows, cols, lds, static_cast<S*>(dst), ldd, grp, half)
+    if (dtype == PPS_DTYPE_BF16) {
+        if (mode == 0) PPS_TR(uint16_t, 0); else if (mode == 1) PPS_TR(uint16_t, 1); else PPS_TR(uint16_t, 2);
+    } else {
+        if (mode == 0) PPS_TR(float, 0); else if (mode == 1) PPS_TR(float, 1); else PPS_TR(float, 2);
+    }
+#undef PPS_TR
     return hipGetLastError();
 }
 

@@ -1,17 +1,25 @@
 // bf16 GEMM on the CDNA4 matrix cores (gfx950), fp32 accumulation.
 //
-// Macro-tile 256 x 256 x 64, 256 threads = 4 wavefronts of 64 lanes laid out
-// 2 x 2; each wavefront owns a 128 x 128 sub-tile = 4 x 4 tiles of
-// v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).
+// Layout: "TN" -- both operands K-contiguous: C[m,n] = sum_k A[m,k] B[n,k],
+// A row-major [M, K] (stride lda), B row-major [N, K] (stride ldb).  The
+// executor stores every operand so that the reduction dimension is
+// contiguous (transposed copies of weights and of the weight-gradient
+// activations), so this one kernel serves all six GEMMs of a SwiGLU block.
 //
-// Data path: global -> registers -> LDS (double buffered, one barrier per K
-// step) -> MFMA operands.  In LDS every operand tile is stored "K-major":
-// 256 rows (M or N) x 64 k of bf16 = 128 bytes per row, in 16-byte chunks of
-// 8 consecutive k, chunk c of row r at position c ^ (r & 7) (XOR swizzle so
-// that the 8 lanes of a ds_read_b128 group hit distinct banks).  Operands
-// whose contiguous dimension is M or N (activations used transposed in the
-// weight-gradient GEMMs, weights [in,out] in the forward) are loaded as 8 x 8
-// bf16 blocks and transposed in registers before the LDS store.
+// Tiling: macro-tile 256 x 256 x 64, 512 threads = 8 wavefronts in a 2 x 4
+// grid, 128 x 64 per wavefront = 4 x 2 tiles of v_mfma_f32_32x32x16_bf16
+// (128 fp32 accumulators per lane, two wavefronts per SIMD).  Eight
+// wavefronts per CU are needed to pull operands from L2 fast enough: with
+// four, a CU sustains about half the bytes per clock the matrix cores
+// consume at this tile size.
+//
+// Data path: global -> LDS by direct-to-LDS buffer loads (no VGPR staging),
+// two 64 KB stages (A and B tiles of 256 rows x 128 bytes), one barrier per
+// K step; MFMA operands are read with ds_read_b128.  In LDS, 16-byte chunk c
+// of row r sits at position c ^ ((r >> 1) & 7), which keeps the 16 lanes of
+// every ds_read_b128 phase on distinct banks (64 banks, two 128-byte rows
+// per bank period).  Buffer loads return zero outside the operand's extent,
+// which pads ragged M, N and K tails without branches.
 //
 // Workgroup -> tile mapping: the dispatcher places workgroup i on XCD i % 8;
 // ids are remapped so each XCD gets a contiguous run of logical tiles, and
@@ -24,23 +32,34 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+#define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 256;
-constexpr int ROWB = BK * 2;            // bytes per LDS tile row
-constexpr int OPB = 256 * ROWB;         // one operand tile: 32 KB
-constexpr int STAGEB = 2 * OPB;         // A + B
-constexpr int LDS_BYTES = 2 * STAGEB;   // two stages: 128 KB
+constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 512, NSTAGE = 2;
+constexpr int ROWB = BK * 2;             // 128 bytes per LDS row
+constexpr int OPB = 256 * ROWB;          // 32 KB per operand tile
+constexpr int STAGEB = 2 * OPB;          // A + B
+constexpr int LDS_BYTES = NSTAGE * STAGEB;
 constexpr int GROUP_M = 8;
+constexpr uint32_t OOB = 0x80000000u;    // an offset past every operand extent
+
+struct Seg {
+    const uint16_t* A;
+    const uint16_t* B;
+    int64_t lda, ldb, K;
+    uint32_t a_bytes, b_bytes;
+};
 
 struct Params {
-    int64_t M, N;
-    int tiles_m, tiles_n, nseg, pad;
-    const uint16_t* A[2];
-    const uint16_t* B[2];
-    const uint16_t* B2[2];
-    int64_t lda[2], ldb[2], K[2];
+    int64_t M, N, NB;      // NB = rows of B
+    int tiles_m, tiles_n, nseg, swiglu;
+    Seg seg[2];
     EpiArgs e;
 };
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
     const int nwg = gridDim.x, bid = blockIdx.x;
@@ -56,144 +75,103 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
     tn = in / gsize;
 }
 
-// K-contiguous operand: 256 rows x 8 chunks; thread t loads chunk (t & 7) of
-// rows (t >> 3) + 32 i.
-__device__ __forceinline__ void load_kc(uint4 (&v)[8], const uint16_t* base, int64_t ld,
-                                        int64_t r0, int64_t nrows, int64_t k0, int64_t K, int t) {
-    const int64_t k = k0 + (t & 7) * 8;
-    const int rr = t >> 3;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t row = r0 + rr + 32 * i;
-        if (k < K && row < nrows) v[i] = *reinterpret_cast<const uint4*>(base + row * ld + k);
-        else v[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
+// s_waitcnt vmcnt(N) with the other counters left at their maximum.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__device__ __forceinline__ void store_kc(const uint4 (&v)[8], char* lds, int t) {
-    const int c = t & 7, rr = t >> 3;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = rr + 32 * i;
-        *reinterpret_cast<uint4*>(lds + row * ROWB + ((c ^ (rr & 7)) << 4)) = v[i];
-    }
-}
-
-// M/N-contiguous operand stored [K][R]: thread t loads the 8 x 8 block of
-// k rows k0 + (t & 7)*8 + j and the 8 columns starting at `col`.
-__device__ __forceinline__ void load_mn(uint4 (&v)[8], const uint16_t* base, int64_t ld,
-                                        int64_t col, bool colok, int64_t k0, int64_t K, int t) {
-    const int64_t kb = k0 + (t & 7) * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int64_t k = kb + j;
-        if (colok && k < K) v[j] = *reinterpret_cast<const uint4*>(base + k * ld + col);
-        else v[j] = make_uint4(0u, 0u, 0u, 0u);
-    }
-}
-
-// Transpose the 8 (k) x 8 (row) block in registers and store 8 chunks.
-__device__ __forceinline__ void store_mn(const uint4 (&v)[8], char* lds, int t) {
-    const int kb = t & 7, rb = t >> 3;
-    uint32_t w[8][4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        w[j][0] = v[j].x; w[j][1] = v[j].y; w[j][2] = v[j].z; w[j][3] = v[j].w;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t d[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t a = w[2 * q][i >> 1], b = w[2 * q + 1][i >> 1];
-            d[q] = (i & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-        }
-        const int row = rb * 8 + i;
-        *reinterpret_cast<uint4*>(lds + row * ROWB + ((kb ^ i) << 4)) = make_uint4(d[0], d[1], d[2], d[3]);
-    }
-}
-
-template <bool AK, bool BKC, bool SWMAP, int EPI>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const Params p) {
-    static_assert(!(SWMAP && BKC), "the SwiGLU column map needs an N-contiguous B");
-    __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+template <int EPI>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
     int tm, tn;
     tile_coords(p, tm, tn);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * (SWMAP ? BN / 2 : BN);
+    const int64_t n0 = (int64_t)tn * (p.swiglu ? BN / 2 : BN);   // first output column
+    const int64_t nb0 = (int64_t)tn * BN;                         // first B row
 
-    f32x16 acc[4][4];
+    // Loader: per K step each wavefront issues 4 A and 4 B direct-to-LDS loads;
+    // load q fills LDS rows (wave*4+q)*8 .. +7 (1 KB); lane l covers row + l/8,
+    // LDS chunk l&7, i.e. logical chunk (l&7) ^ ((row>>1)&7).
+    const int lrow = lane >> 3;
+    int lcq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lcq[q] = (lane & 7) ^ (((wave * 4 + q) * 4 + (lane >> 4)) & 7);
+    uint32_t aoff[2][4], boff[2][4];
+    rsrc_t ar[2], br[2];
+    int nkt[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const Seg& g = p.seg[s < p.nseg ? s : 0];
+        ar[s] = make_rsrc(g.A, g.a_bytes);
+        br[s] = make_rsrc(g.B, g.b_bytes);
+        nkt[s] = s < p.nseg ? (int)((g.K + BK - 1) / BK) : 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = (wave * 4 + q) * 8 + lrow;
+            const int64_t ra = m0 + row, rb = nb0 + row;
+            aoff[s][q] = ra < p.M ? (uint32_t)(ra * g.lda * 2 + lcq[q] * 16) : OOB;
+            boff[s][q] = rb < p.NB ? (uint32_t)(rb * g.ldb * 2 + lcq[q] * 16) : OOB;
+        }
+    }
+    const int nk = nkt[0] + nkt[1];
+
+    auto issue = [&](int kt) {
+        const int s = kt < nkt[0] ? 0 : 1;
+        const int64_t k0 = (int64_t)(kt - (s ? nkt[0] : 0)) * BK;
+        char* st = smem + (kt % NSTAGE) * STAGEB;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool kv = k0 + lcq[q] * 8 < p.seg[s].K;
+            const uint32_t ao = (kv && aoff[s][q] != OOB) ? aoff[s][q] + (uint32_t)(k0 * 2) : OOB;
+            const uint32_t bo = (kv && boff[s][q] != OOB) ? boff[s][q] + (uint32_t)(k0 * 2) : OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(s ? ar[1] : ar[0], (LDS_AS void*)(st + (wave * 4 + q) * 1024), 16, ao, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(s ? br[1] : br[0], (LDS_AS void*)(st + OPB + (wave * 4 + q) * 1024), 16, bo, 0, 0, 0);
+        }
+    };
+
+    // MFMA operand fragment: row r, logical chunk ch at r*128 + (ch ^ ((r>>1)&7))*16.
+    const int fsw = ((lane & 31) >> 1) & 7;
+    auto frags = [&](int kt, int kk, bf16x8 (&a)[4], bf16x8 (&b)[2]) {
+        const char* st = smem + (kt % NSTAGE) * STAGEB;
+        const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) << 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            a[i] = *reinterpret_cast<const bf16x8*>(st + (wm * 128 + i * 32 + (lane & 31)) * ROWB + pc);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            b[j] = *reinterpret_cast<const bf16x8*>(st + OPB + (wn * 64 + j * 32 + (lane & 31)) * ROWB + pc);
+    };
+
+    f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    for (int s = 0; s < p.nseg; ++s) {
-        const int64_t K = p.K[s];
-        const int nk = (int)((K + BK - 1) / BK);
-        if (nk == 0) continue;
-        const uint16_t* A = p.A[s];
-        const int64_t lda = p.lda[s], ldb = p.ldb[s];
-
-        // Per-thread column block for M/N-contiguous operands.
-        const int cb = (t >> 3) * 8;
-        const int64_t acol = m0 + cb;
-        const bool acolok = acol < p.M;
-        const uint16_t* bbase = p.B[s];
-        int64_t bcol = n0 + cb;
-        if constexpr (SWMAP) {
-            // tile column c -> group c/128; first 64 from B (gate), next 64 from B2 (up)
-            const int grp = cb >> 7, w = cb & 127;
-            bbase = (w >= 64) ? p.B2[s] : p.B[s];
-            bcol = n0 + grp * 64 + (w & 63);
-        }
-        const bool bcolok = bcol < p.N;
-
-        uint4 ra[8], rb[8];
-        auto gload = [&](int kt) {
-            const int64_t k0 = (int64_t)kt * BK;
-            if constexpr (AK) load_kc(ra, A, lda, m0, p.M, k0, K, t);
-            else load_mn(ra, A, lda, acol, acolok, k0, K, t);
-            if constexpr (BKC) load_kc(rb, p.B[s], ldb, n0, p.N, k0, K, t);
-            else load_mn(rb, bbase, ldb, bcol, bcolok, k0, K, t);
-        };
-        auto lstore = [&](int buf) {
-            char* la = smem + buf * STAGEB;
-            if constexpr (AK) store_kc(ra, la, t); else store_mn(ra, la, t);
-            if constexpr (BKC) store_kc(rb, la + OPB, t); else store_mn(rb, la + OPB, t);
-        };
-
-        gload(0);
-        lstore(0);
+    if (nk > 0) {
+        issue(0);
+        wait_vm<0>();
         __syncthreads();
+        bf16x8 fa[2][4], fb[2][2];
         for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < nk) gload(kt + 1);
-            const char* la = smem + cur * STAGEB;
-            const char* lb = la + OPB;
+            if (kt + 1 < nk) issue(kt + 1);   // into the other stage, freed by the last barrier
+            frags(kt, 0, fa[0], fb[0]);
 #pragma unroll
             for (int kk = 0; kk < BK / 16; ++kk) {
-                const int ch = kk * 2 + (lane >> 5);
-                const int sw = (ch ^ (lane & 7)) << 4;
-                bf16x8 a[4], b[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a[i] = *reinterpret_cast<const bf16x8*>(la + (wm * 128 + i * 32 + (lane & 31)) * ROWB + sw);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    b[j] = *reinterpret_cast<const bf16x8*>(lb + (wn * 128 + j * 32 + (lane & 31)) * ROWB + sw);
+                if (kk + 1 < BK / 16) frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
             }
-            if (kt + 1 < nk) lstore(cur ^ 1);
+            wait_vm<0>();
             __syncthreads();
         }
     }
@@ -207,15 +185,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const Params p) 
             const int64_t row = m0 + wm * 128 + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
             const bool rok = row < p.M;
             if constexpr (EPI == EPI_SWIGLU) {
+                // a wavefront's 64 B rows are 32 gate rows then 32 up rows of the
+                // same 32 hidden columns
+                const int64_t col = n0 + wn * 32 + (lane & 31);
+                if (rok && col < p.N) epi_swiglu<uint16_t>(p.e, row, col, acc[i][0][e], acc[i][1][e]);
+            } else {
 #pragma clang loop unroll(full)
                 for (int j = 0; j < 2; ++j) {
                     const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
-                    if (rok && col < p.N) epi_swiglu<uint16_t>(p.e, row, col, acc[i][j][e], acc[i][j + 2][e]);
-                }
-            } else {
-#pragma clang loop unroll(full)
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
                     if (rok && col < p.N) epi_apply<EPI, uint16_t>(p.e, row, col, acc[i][j][e]);
                 }
             }
@@ -223,46 +200,60 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_bf16_kernel(const Params p) 
     }
 }
 
-template <bool AK, bool BKC, bool SWMAP, int EPI>
+// Byte extent of a row-major operand: (rows-1)*ld + cols elements of bf16.
+inline bool extent(int64_t rows, int64_t ld, int64_t cols, uint32_t& out) {
+    const int64_t b = rows <= 0 ? 0 : ((rows - 1) * ld + cols) * 2;
+    if (b >= (int64_t)OOB) return false;
+    out = (uint32_t)b;
+    return true;
+}
+
+template <int EPI>
 hipError_t launch(const Params& p, hipStream_t s) {
-    const int grid = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((gemm_bf16_kernel<AK, BKC, SWMAP, EPI>), dim3(grid), dim3(NTHREADS), 0, s, p);
+    hipLaunchKernelGGL((gemm_tn_kernel<EPI>), dim3(p.tiles_m * p.tiles_n), dim3(NTHREADS), 0, s, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
+int64_t swiglu_b_rows(int64_t ffn) { return 2 * ((ffn + 31) / 32) * 32; }
+
+// Requires K-contiguous A and B, 16-byte aligned rows, every operand extent
+// under 2 GB.  With the SwiGLU map, B is the gate/up weight interleaved per 32
+// hidden columns (32 gate rows, then 32 up rows; swiglu_b_rows(N) rows) and N
+// is the number of hidden columns.
 hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
+    if (!a.a_kcontig || !a.b_kcontig) return hipErrorInvalidValue;
     Params p{};
     p.M = a.M;
     p.N = a.N;
     p.nseg = a.nseg;
+    p.swiglu = a.swiglu_map ? 1 : 0;
+    const int64_t cols_per_tile = a.swiglu_map ? BN / 2 : BN;
+    p.tiles_m = (int)((a.M + BM - 1) / BM);
+    p.tiles_n = (int)((a.N + cols_per_tile - 1) / cols_per_tile);
+    p.NB = a.swiglu_map ? swiglu_b_rows(a.N) : a.N;
     for (int i = 0; i < a.nseg; ++i) {
-        p.A[i] = static_cast<const uint16_t*>(a.seg[i].A);
-        p.B[i] = static_cast<const uint16_t*>(a.seg[i].B);
-        p.B2[i] = static_cast<const uint16_t*>(a.seg[i].B2);
-        p.lda[i] = a.seg[i].lda;
-        p.ldb[i] = a.seg[i].ldb;
-        p.K[i] = a.seg[i].K;
+        const GemmSeg& g = a.seg[i];
+        p.seg[i].A = static_cast<const uint16_t*>(g.A);
+        p.seg[i].B = static_cast<const uint16_t*>(g.B);
+        p.seg[i].lda = g.lda;
+        p.seg[i].ldb = g.ldb;
+        p.seg[i].K = g.K;
+        if (!extent(a.M, g.lda, g.K, p.seg[i].a_bytes) || !extent(p.NB, g.ldb, g.K, p.seg[i].b_bytes))
+            return hipErrorInvalidValue;
     }
     p.e = a.e;
-    const int64_t ncols_per_tile = a.swiglu_map ? BN / 2 : BN;
-    p.tiles_m = (int)((a.M + BM - 1) / BM);
-    p.tiles_n = (int)((a.N + ncols_per_tile - 1) / ncols_per_tile);
     if (p.tiles_m == 0 || p.tiles_n == 0) return hipSuccess;
-
-#define PPS_GEMM_CASE(AKV, BKV, SWV, EPV)                                                  \
-    if (a.a_kcontig == AKV && a.b_kcontig == BKV && a.swiglu_map == SWV && a.epi == EPV) \
-        return launch<AKV, BKV, SWV, EPV>(p, s);
-    PPS_GEMM_CASE(true, false, true, EPI_SWIGLU)        // g,u = n [Wg|Wu]
-    PPS_GEMM_CASE(true, false, false, EPI_RESID)        // y = x + h Wd
-    PPS_GEMM_CASE(true, true, false, EPI_SWIGLU_BWD)    // dh = dy Wd^T
-    PPS_GEMM_CASE(true, true, false, EPI_STORE_F32)     // dn = dg Wg^T + du Wu^T
-    PPS_GEMM_CASE(false, false, false, EPI_ACC_F32)     // dW += X^T G
-    PPS_GEMM_CASE(true, false, false, EPI_STORE)
-    PPS_GEMM_CASE(true, true, false, EPI_STORE)
-#undef PPS_GEMM_CASE
-    return hipErrorInvalidValue;
+    switch (a.epi) {
+        case EPI_SWIGLU: return launch<EPI_SWIGLU>(p, s);
+        case EPI_RESID: return launch<EPI_RESID>(p, s);
+        case EPI_SWIGLU_BWD: return launch<EPI_SWIGLU_BWD>(p, s);
+        case EPI_STORE_F32: return launch<EPI_STORE_F32>(p, s);
+        case EPI_ACC_F32: return launch<EPI_ACC_F32>(p, s);
+        case EPI_STORE: return launch<EPI_STORE>(p, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace pps

@@ -84,6 +84,17 @@ hipError_t gelu_bwd(const float* dy, const float* z, int64_t count, float* dz, h
 // out[j] += sum_t a[t, j]  (fp32, fixed order)
 hipError_t colsum_acc(const float* a, int64_t T, int64_t d, float* out, hipStream_t s);
 
+// Tiled transpose: dst[map(c), r] = f(src[r, c]) for r < rows, c < cols;
+// dst columns in [rows, ldd) are zeroed.  mode 0: copy; 1: (src r[row]) gamma[c];
+// 2: silu(src) src2.  map(c) = c, or (c/grp)*2grp + half*grp + c%grp with grp > 0.
+// cols, lds and ldd must be multiples of 8.
+hipError_t transpose(int dtype, int mode, const void* src, const void* src2, const float* r, const float* gamma,
+                     int64_t rows, int64_t cols, int64_t lds, void* dst, int64_t ldd, int grp, int half,
+                     hipStream_t s);
+
+// Rows of the interleaved gate/up weight copy used by the forward GEMM.
+int64_t swiglu_b_rows(int64_t ffn);
+
 // dst = src * scale (n elements of the storage type)
 hipError_t scale(int dtype, void* dst, const void* src, int64_t n, float scale, hipStream_t s);
 

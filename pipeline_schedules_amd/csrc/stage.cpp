@@ -70,6 +70,15 @@ struct pps_stage {
     char* scratch = nullptr;
     size_t scratch_bytes = 0;
     size_t s_n = 0, s_h = 0, s_dgu = 0, s_dn = 0, s_dxa = 0, s_dxb = 0, s_part = 0, s_dz = 0;
+    // bf16 path: K-contiguous operands of the weight-gradient GEMMs ([feature, Tp])
+    size_t s_nT = 0, s_hT = 0, s_dguT = 0, s_dyT = 0;
+    int64_t Tp = 0;                   // T rounded up to a multiple of 8
+    bool tn = false;                  // bf16 path: every GEMM runs with K-contiguous operands
+    // bf16 path: per-pass copies of the forward weights, [chunk*L + block]:
+    // WguT (swiglu_b_rows(ffn) x d, gate/up interleaved per 32) and WdT (d x ffn)
+    char* wcopy = nullptr;
+    size_t wcopy_bytes = 0;
+    std::vector<size_t> wgu_off, wd_off;
     float* grads = nullptr;
     size_t grad_bytes = 0;
     std::vector<size_t> goff;         // [(chunk*L + block)*4 + which] element offsets
@@ -120,7 +129,9 @@ hipError_t timed(pps_stage* h, int kernel, double flops, double bytes, F&& launc
         }                                      \
     } while (0)
 
-Layout make_layout(const pps_stage_desc& d, bool swiglu, bool split, int es) {
+// With tn (bf16 path) the split extras are the transposed dg|du [2 ffn, Tp]
+// and dy [d, Tp] that the deferred weight-gradient GEMMs read.
+Layout make_layout(const pps_stage_desc& d, bool swiglu, bool split, int es, bool tn, int64_t Tp) {
     Layout L;
     const size_t T = (size_t)d.T, dm = (size_t)d.d, f = (size_t)d.ffn;
     size_t off = 0;
@@ -141,8 +152,8 @@ Layout make_layout(const pps_stage_desc& d, bool swiglu, bool split, int es) {
     if (split) {
         for (int b = 0; b < nb; ++b) {
             if (swiglu) {
-                take(L.dgu, T * 2 * f * es);
-                take(L.dy, T * dm * es);
+                take(L.dgu, (tn ? (size_t)Tp : T) * 2 * f * es);
+                take(L.dy, (tn ? (size_t)Tp : T) * dm * es);
             } else {
                 take(L.dz, T * dm * 4);
             }
@@ -178,6 +189,7 @@ void release(pps_stage* h) {
     if (h->pool) hipFree(h->pool);
     if (h->scratch) hipFree(h->scratch);
     if (h->grads) hipFree(h->grads);
+    if (h->wcopy) hipFree(h->wcopy);
     delete h;
 }
 
@@ -209,6 +221,28 @@ double gemm_flops(double M, double N, double K) { return 2.0 * M * N * K; }
 
 // ---- SwiGLU block sequences ------------------------------------------------
 
+// bf16 path: refresh the K-contiguous copies of the forward weights from the
+// caller's Wg, Wu ([d, ffn]) and Wd ([ffn, d]).  Done once at the start of
+// every pass, so weights updated between passes are picked up.
+int refresh_weight_copies(pps_stage* h) {
+    const pps_stage_desc& D = h->d;
+    const int64_t d = D.d, f = D.ffn;
+    for (int i = 0; i < D.v * D.L; ++i) {
+        const void* const* wb = h->w.data() + (size_t)i * 4;
+        char* wgu = h->wcopy + h->wgu_off[i];
+        char* wdt = h->wcopy + h->wd_off[i];
+        PPS_TRY(timed(h, PPS_K_COPY, 0.0, 4.0 * d * f * 2, [&] {
+            hipError_t e = pps::transpose(D.dtype, 0, wb[0], nullptr, nullptr, nullptr, d, f, f, wgu, d, 32, 0, h->stream);
+            if (e == hipSuccess) e = pps::transpose(D.dtype, 0, wb[1], nullptr, nullptr, nullptr, d, f, f, wgu, d, 32, 1, h->stream);
+            return e;
+        }));
+        PPS_TRY(timed(h, PPS_K_COPY, 0.0, 2.0 * d * f * 2, [&] {
+            return pps::transpose(D.dtype, 0, wb[2], nullptr, nullptr, nullptr, f, d, d, wdt, f, 0, 0, h->stream);
+        }));
+    }
+    return PPS_OK;
+}
+
 int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_out) {
     const pps_stage_desc& D = h->d;
     const int64_t T = D.T, d = D.d, f = D.ffn;
@@ -216,8 +250,9 @@ int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_
     char* sb = slot_base(h, slot);
     char* sn = h->scratch + h->s_n;
     char* sh = h->scratch + h->s_h;
+    const int blk0 = chunk * D.L;
     for (int b = 0; b < D.L; ++b) {
-        const void* const* wb = h->w.data() + (size_t)(chunk * D.L + b) * 4;
+        const void* const* wb = h->w.data() + (size_t)(blk0 + b) * 4;
         const float* gamma = static_cast<const float*>(wb[3]);
         char* xb = sb + h->lay.x[b];
         float* rb = reinterpret_cast<float*>(sb + h->lay.r[b]);
@@ -232,8 +267,12 @@ int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_
         GemmArgs a;
         a.M = T; a.N = f; a.nseg = 1;
         a.seg[0].A = sn; a.seg[0].lda = d; a.seg[0].K = d;
-        a.seg[0].B = wb[0]; a.seg[0].B2 = wb[1]; a.seg[0].ldb = f;
-        a.a_kcontig = true; a.b_kcontig = false; a.swiglu_map = true;
+        a.a_kcontig = true; a.swiglu_map = true;
+        if (h->tn) {
+            a.seg[0].B = h->wcopy + h->wgu_off[blk0 + b]; a.seg[0].ldb = d; a.b_kcontig = true;
+        } else {
+            a.seg[0].B = wb[0]; a.seg[0].B2 = wb[1]; a.seg[0].ldb = f; a.b_kcontig = false;
+        }
         a.epi = pps::EPI_SWIGLU;
         a.e.out0 = gb; a.e.out1 = ub; a.e.out2 = sh; a.e.ld0 = f;
         PPS_TRY(timed(h, PPS_K_GATEUP, gemm_flops(T, 2.0 * f, d), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
@@ -241,8 +280,12 @@ int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_
         GemmArgs c;
         c.M = T; c.N = d; c.nseg = 1;
         c.seg[0].A = sh; c.seg[0].lda = f; c.seg[0].K = f;
-        c.seg[0].B = wb[2]; c.seg[0].ldb = d;
-        c.a_kcontig = true; c.b_kcontig = false;
+        c.a_kcontig = true;
+        if (h->tn) {
+            c.seg[0].B = h->wcopy + h->wd_off[blk0 + b]; c.seg[0].ldb = f; c.b_kcontig = true;
+        } else {
+            c.seg[0].B = wb[2]; c.seg[0].ldb = d; c.b_kcontig = false;
+        }
         c.epi = pps::EPI_RESID;
         c.e.out0 = b == D.L - 1 ? y_out : static_cast<void*>(sb + h->lay.x[b + 1]);
         c.e.ld0 = d; c.e.in0 = xb; c.e.ldi0 = d;
@@ -251,38 +294,66 @@ int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_
     return PPS_OK;
 }
 
+// bf16 path: write the transposed dy [d, Tp] and dg|du [2 ffn, Tp] that the
+// weight-gradient GEMMs read with K = T contiguous.
+int swiglu_stage_w_operands(pps_stage* h, const void* dy, const void* dgu, void* dyT, void* dguT) {
+    const pps_stage_desc& D = h->d;
+    const int64_t T = D.T, d = D.d, f = D.ffn, Tp = h->Tp;
+    PPS_TRY(timed(h, PPS_K_COPY, 0.0, (double)(T + Tp) * d * 2, [&] {
+        return pps::transpose(D.dtype, 0, dy, nullptr, nullptr, nullptr, T, d, d, dyT, Tp, 0, 0, h->stream);
+    }));
+    PPS_TRY(timed(h, PPS_K_COPY, 0.0, (double)(T + Tp) * 2 * f * 2, [&] {
+        return pps::transpose(D.dtype, 0, dgu, nullptr, nullptr, nullptr, T, 2 * f, 2 * f, dguT, Tp, 0, 0, h->stream);
+    }));
+    return PPS_OK;
+}
+
 // Weight gradient of block b: dWd += h^T dy; dWg += n^T dg; dWu += n^T du,
-// with n and h recomputed from the stash.
+// with n and h recomputed from the stash.  bf16 path: dy and dgu are the
+// transposed [d, Tp] and [2 ffn, Tp] copies; fp32 path: row-major [T, .].
 int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, const void* dgu) {
     const pps_stage_desc& D = h->d;
-    const int64_t T = D.T, d = D.d, f = D.ffn;
+    const int64_t T = D.T, d = D.d, f = D.ffn, Tp = h->Tp;
     const int dt = D.dtype, es = h->es;
     char* sb = slot_base(h, slot);
-    char* sn = h->scratch + h->s_n;
-    char* sh = h->scratch + h->s_h;
     const void* const* wb = h->w.data() + (size_t)(chunk * D.L + b) * 4;
     const float* gamma = static_cast<const float*>(wb[3]);
     const size_t gi = (size_t)(chunk * D.L + b) * 4;
     float* dWg = h->grads + h->goff[gi + 0];
     float* dWu = h->grads + h->goff[gi + 1];
     float* dWd = h->grads + h->goff[gi + 2];
-    PPS_TRY(timed(h, PPS_K_PREP_W, 0.0, (double)T * (2.0 * d + 3.0 * f) * es + T * 4.0 + d * 4.0, [&] {
-        return pps::prep_w(dt, sb + h->lay.x[b], reinterpret_cast<const float*>(sb + h->lay.r[b]), gamma,
-                           sb + h->lay.g[b], sb + h->lay.u[b], T, d, f, sn, sh, h->stream);
-    }));
-    GemmArgs a;
-    a.M = f; a.N = d; a.nseg = 1;
-    a.seg[0].A = sh; a.seg[0].lda = f; a.seg[0].K = T;
-    a.seg[0].B = dy; a.seg[0].ldb = d;
-    a.a_kcontig = false; a.b_kcontig = false;
+    const char* xb = sb + h->lay.x[b];
+    const float* rb = reinterpret_cast<const float*>(sb + h->lay.r[b]);
+    GemmArgs a, c;
+    if (h->tn) {
+        char* nT = h->scratch + h->s_nT;
+        char* hT = h->scratch + h->s_hT;
+        PPS_TRY(timed(h, PPS_K_PREP_W, 0.0, (double)T * (2.0 * d + 2.0 * f) * es + (double)Tp * (d + f) * es, [&] {
+            hipError_t e = pps::transpose(dt, 1, xb, nullptr, rb, gamma, T, d, d, nT, Tp, 0, 0, h->stream);
+            if (e == hipSuccess)
+                e = pps::transpose(dt, 2, sb + h->lay.g[b], sb + h->lay.u[b], nullptr, nullptr, T, f, f, hT, Tp, 0, 0, h->stream);
+            return e;
+        }));
+        a.seg[0].A = hT; a.seg[0].lda = Tp; a.seg[0].B = dy; a.seg[0].ldb = Tp;
+        a.b_kcontig = true; a.a_kcontig = true;
+        c.seg[0].A = nT; c.seg[0].lda = Tp; c.seg[0].B = dgu; c.seg[0].ldb = Tp;
+        c.b_kcontig = true; c.a_kcontig = true;
+    } else {
+        char* sn = h->scratch + h->s_n;
+        char* sh = h->scratch + h->s_h;
+        PPS_TRY(timed(h, PPS_K_PREP_W, 0.0, (double)T * (2.0 * d + 3.0 * f) * es + T * 4.0 + d * 4.0, [&] {
+            return pps::prep_w(dt, xb, rb, gamma, sb + h->lay.g[b], sb + h->lay.u[b], T, d, f, sn, sh, h->stream);
+        }));
+        a.seg[0].A = sh; a.seg[0].lda = f; a.seg[0].B = dy; a.seg[0].ldb = d;
+        a.a_kcontig = false; a.b_kcontig = false;
+        c.seg[0].A = sn; c.seg[0].lda = d; c.seg[0].B = dgu; c.seg[0].ldb = 2 * f;
+        c.a_kcontig = false; c.b_kcontig = false;
+    }
+    a.M = f; a.N = d; a.nseg = 1; a.seg[0].K = T;
     a.epi = pps::EPI_ACC_F32;
     a.e.out0 = dWd; a.e.ld0 = d; a.e.nsplit = d;
     PPS_TRY(timed(h, PPS_K_WGRAD_DOWN, gemm_flops(f, d, T), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
-    GemmArgs c;
-    c.M = d; c.N = 2 * f; c.nseg = 1;
-    c.seg[0].A = sn; c.seg[0].lda = d; c.seg[0].K = T;
-    c.seg[0].B = dgu; c.seg[0].ldb = 2 * f;
-    c.a_kcontig = false; c.b_kcontig = false;
+    c.M = d; c.N = 2 * f; c.nseg = 1; c.seg[0].K = T;
     c.epi = pps::EPI_ACC_F32;
     c.e.out0 = dWg; c.e.ld0 = f; c.e.out1 = dWu; c.e.ld1 = f; c.e.nsplit = f;
     PPS_TRY(timed(h, PPS_K_WGRAD_GATEUP, gemm_flops(d, 2.0 * f, T), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
@@ -297,7 +368,7 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
     char* dxbuf[2] = {h->scratch + h->s_dxa, h->scratch + h->s_dxb};
     float* dn = reinterpret_cast<float*>(h->scratch + h->s_dn);
     float* part = reinterpret_cast<float*>(h->scratch + h->s_part);
-    if (h->split) {
+    if (h->split && !h->tn) {
         // Keep this micro-batch's output gradient for the deferred W.
         char* dst = sb + h->lay.dy[D.L - 1];
         PPS_TRY(timed(h, PPS_K_COPY, 0.0, 2.0 * T * d * es, [&] { return pps::copy_bytes(dst, dy_in, T * d * es, h->stream); }));
@@ -310,7 +381,7 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
         const void* dy;
         void* dx;
         char* dgu;
-        if (h->split) {
+        if (h->split && !h->tn) {
             dy = sb + h->lay.dy[b];
             dx = b == 0 ? dx_out : static_cast<void*>(sb + h->lay.dy[b - 1]);
             dgu = sb + h->lay.dgu[b];
@@ -338,6 +409,18 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
         c.epi = pps::EPI_STORE_F32;
         c.e.out0 = dn; c.e.ld0 = d;
         PPS_TRY(timed(h, PPS_K_DN, gemm_flops(T, d, 2.0 * f), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
+        // bf16: the W GEMMs read dy and dg|du transposed; keep them (split: in
+        // the stash until W) before dy's buffer is reused.
+        const void* wdy = dy;
+        const void* wdgu = dgu;
+        if (h->tn) {
+            void* dyT = h->split ? static_cast<void*>(sb + h->lay.dy[b]) : static_cast<void*>(h->scratch + h->s_dyT);
+            void* dguT = h->split ? static_cast<void*>(sb + h->lay.dgu[b]) : static_cast<void*>(h->scratch + h->s_dguT);
+            int rc = swiglu_stage_w_operands(h, dy, dgu, dyT, dguT);
+            if (rc != PPS_OK) return rc;
+            wdy = dyT;
+            wdgu = dguT;
+        }
         // RMSNorm backward + residual, dgamma partials, then their fixed-order sum.
         int nrows = 0;
         PPS_TRY(timed(h, PPS_K_RMSNORM_BWD, 0.0,
@@ -350,7 +433,7 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
             return pps::column_reduce_acc(part, T > 0 ? prow : 0, d, dgam, h->stream);
         }));
         if (!h->split) {
-            int rc = swiglu_weight(h, slot, chunk, b, dy, dgu);
+            int rc = swiglu_weight(h, slot, chunk, b, wdy, wdgu);
             if (rc != PPS_OK) return rc;
         }
     }
@@ -483,16 +566,32 @@ extern "C" int pps_stage_create(const pps_stage_desc* desc, pps_stage** out) {
     h->slot_of.assign((size_t)desc->M * desc->v, -1);
     h->slot_used.assign(h->S, 0);
 
-    h->lay = make_layout(*desc, h->swiglu, h->split, h->es);
-    const size_t T = (size_t)desc->T, dm = (size_t)desc->d, f = (size_t)desc->ffn;
+    h->tn = h->swiglu && desc->dtype == PPS_DTYPE_BF16;
+    h->Tp = (desc->T + 7) / 8 * 8;
+    h->lay = make_layout(*desc, h->swiglu, h->split, h->es, h->tn, h->Tp);
+    const size_t T = (size_t)desc->T, dm = (size_t)desc->d, f = (size_t)desc->ffn, Tp = (size_t)h->Tp;
     size_t off = 0;
     auto take = [&](size_t& o, size_t bytes) { o = off; off += align256(bytes); };
     if (h->swiglu) {
         take(h->s_n, T * dm * h->es);
         take(h->s_h, T * f * h->es);
-        take(h->s_dgu, h->split ? 256 : T * 2 * f * h->es);
+        take(h->s_dgu, (h->split && !h->tn) ? 256 : T * 2 * f * h->es);
         take(h->s_dn, T * dm * 4);
         take(h->s_part, (size_t)pps::rmsnorm_bwd_partial_rows((int64_t)T) * dm * 4);
+        if (h->tn) {
+            take(h->s_nT, dm * Tp * 2);
+            take(h->s_hT, f * Tp * 2);
+            take(h->s_dguT, h->split ? 256 : 2 * f * Tp * 2);
+            take(h->s_dyT, h->split ? 256 : dm * Tp * 2);
+            size_t w = 0;
+            for (int i = 0; i < desc->v * desc->L; ++i) {
+                h->wgu_off.push_back(w);
+                w += align256((size_t)pps::swiglu_b_rows(desc->ffn) * dm * 2);
+                h->wd_off.push_back(w);
+                w += align256(dm * f * 2);
+            }
+            h->wcopy_bytes = w;
+        }
     } else {
         take(h->s_dz, T * dm * 4);
     }
@@ -521,18 +620,21 @@ extern "C" int pps_stage_create(const pps_stage_desc* desc, pps_stage** out) {
     h->st.n_slots = h->S;
     h->st.slot_bytes = (int64_t)h->lay.slot_bytes;
     h->st.pool_bytes = (int64_t)h->lay.slot_bytes * h->S;
-    h->st.scratch_bytes = (int64_t)h->scratch_bytes;
+    h->st.scratch_bytes = (int64_t)(h->scratch_bytes + h->wcopy_bytes);
     h->st.grad_bytes = (int64_t)h->grad_bytes;
 
     if (!h->bookkeeping) {
         if (hipMalloc(reinterpret_cast<void**>(&h->pool), std::max<size_t>(h->lay.slot_bytes * h->S, 256)) != hipSuccess ||
             hipMalloc(reinterpret_cast<void**>(&h->scratch), h->scratch_bytes) != hipSuccess ||
-            hipMalloc(reinterpret_cast<void**>(&h->grads), std::max<size_t>(h->grad_bytes, 256)) != hipSuccess) {
+            hipMalloc(reinterpret_cast<void**>(&h->grads), std::max<size_t>(h->grad_bytes, 256)) != hipSuccess ||
+            (h->wcopy_bytes && hipMalloc(reinterpret_cast<void**>(&h->wcopy), h->wcopy_bytes) != hipSuccess)) {
             (void)hipGetLastError();
             release(h);
             return PPS_ENOMEM;
         }
         if (pps::fill_zero(h->grads, (int64_t)h->grad_bytes, h->stream) != hipSuccess) { release(h); return PPS_EHIP; }
+        // the padding rows of the interleaved gate/up copy must read as zero
+        if (h->wcopy && pps::fill_zero(h->wcopy, (int64_t)h->wcopy_bytes, h->stream) != hipSuccess) { release(h); return PPS_EHIP; }
         if (h->profile) {
             const int cap = desc->profile_capacity;
             h->ev.assign((size_t)cap * 2, nullptr);
@@ -553,13 +655,20 @@ extern "C" int pps_stage_forward(pps_stage* h, int mb, int chunk, const void* x_
     if (h->failed) return PPS_EHIP;
     if (mb < 0 || mb >= h->d.M || chunk < 0 || chunk >= h->d.v) return PPS_EINVAL;
     if (!h->bookkeeping && (!x_in || !y_out)) return PPS_EINVAL;
-    maybe_new_pass(h);
-    if (h->fpos >= h->fseq.size() || h->fseq[h->fpos] != std::make_pair(mb, chunk)) return PPS_EORDER;
+    // A call after a completed pass starts the next one.
+    const bool next_pass = h->fpos == h->fseq.size() && h->bpos == h->bseq.size() && h->wpos == h->wseq.size();
+    const size_t fpos = next_pass ? 0 : h->fpos;
+    if (fpos >= h->fseq.size() || h->fseq[fpos] != std::make_pair(mb, chunk)) return PPS_EORDER;
     int slot = 0;
     while (slot < h->S && h->slot_used[slot]) ++slot;
     if (slot == h->S) return PPS_EFULL;
+    if (next_pass) maybe_new_pass(h);
 
     if (!h->bookkeeping) {
+        if (h->tn && h->fpos == 0) {
+            int rc = refresh_weight_copies(h);
+            if (rc != PPS_OK) return rc;
+        }
         int rc = h->swiglu ? swiglu_forward(h, slot, chunk, x_in, y_out) : toy_forward(h, slot, chunk, x_in, y_out);
         if (rc != PPS_OK) return rc;
     }
