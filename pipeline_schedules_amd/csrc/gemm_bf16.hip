@@ -75,6 +75,90 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
     tn = in / gsize;
 }
 
+// ---- epilogue ---------------------------------------------------------------
+// A 32x32 MFMA accumulator gives lane l column l%32 and, for element group q,
+// rows q*8 + (l/32)*4 + 0..3.  A 4x4 transpose inside each lane quad (DPP quad
+// permutes) turns that into row q*8 + (l/32)*4 + l%4 and columns 4*(l%32/4) +
+// 0..3, so every global access of the epilogue is an 8-byte (bf16) or 16-byte
+// (fp32) vector and one wavefront access covers 8 rows x 32 columns.
+
+__device__ __forceinline__ float sel4(const float (&v)[4], int i) {
+    return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+
+template <int CTRL>
+__device__ __forceinline__ float quad_xor(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// v: this lane's 4 rows at its column; w: this lane's row, 4 columns.
+__device__ __forceinline__ void quad_transpose(const float (&v)[4], float (&w)[4], int j) {
+    float r[4];
+    r[0] = sel4(v, j);
+    r[1] = quad_xor<0xB1>(sel4(v, j ^ 1));   // from lane j^1
+    r[2] = quad_xor<0x4E>(sel4(v, j ^ 2));   // from lane j^2
+    r[3] = quad_xor<0x1B>(sel4(v, j ^ 3));   // from lane j^3
+#pragma unroll
+    for (int m = 0; m < 4; ++m) w[m] = sel4(r, m ^ j);
+}
+
+__device__ __forceinline__ uint2 pack4(const float (&w)[4]) {
+    return make_uint2(f2bf(w[0]) | (f2bf(w[1]) << 16), f2bf(w[2]) | (f2bf(w[3]) << 16));
+}
+
+__device__ __forceinline__ void unpack4(uint2 q, float (&w)[4]) {
+    w[0] = bf2f(q.x & 0xffffu); w[1] = bf2f(q.x >> 16);
+    w[2] = bf2f(q.y & 0xffffu); w[3] = bf2f(q.y >> 16);
+}
+
+// Four consecutive output columns col..col+3 of one row.
+template <int EPI>
+__device__ __forceinline__ void epi4(const EpiArgs& e, int64_t row, int64_t col, const float (&w)[4]) {
+    if constexpr (EPI == EPI_STORE_F32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(e.out0) + row * e.ld0 + col) = make_float4(w[0], w[1], w[2], w[3]);
+    } else if constexpr (EPI == EPI_STORE) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out0) + row * e.ld0 + col) = pack4(w);
+    } else if constexpr (EPI == EPI_RESID) {
+        float x[4], y[4];
+        unpack4(*reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(e.in0) + row * e.ldi0 + col), x);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) y[k] = x[k] + w[k];
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out0) + row * e.ld0 + col) = pack4(y);
+    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+        float g[4], u[4], dg[4], du[4];
+        unpack4(*reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(e.in0) + row * e.ldi0 + col), g);
+        unpack4(*reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(e.in1) + row * e.ldi0 + col), u);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) swiglu_bwd_f(w[k], g[k], u[k], dg[k], du[k]);
+        uint16_t* o = static_cast<uint16_t*>(e.out0) + row * e.ld0;
+        *reinterpret_cast<uint2*>(o + col) = pack4(dg);
+        *reinterpret_cast<uint2*>(o + e.nsplit + col) = pack4(du);
+    } else if constexpr (EPI == EPI_ACC_F32) {
+        float* o = col < e.nsplit ? static_cast<float*>(e.out0) + row * e.ld0 + col
+                                  : static_cast<float*>(e.out1) + row * e.ld1 + (col - e.nsplit);
+        float4 a = *reinterpret_cast<const float4*>(o);
+        a.x += w[0]; a.y += w[1]; a.z += w[2]; a.w += w[3];
+        *reinterpret_cast<float4*>(o) = a;
+    }
+}
+
+// Gate/up pair for hidden columns col..col+3: stores g, u (bf16) and
+// h = silu(g) u computed from the stored values.
+__device__ __forceinline__ void epi4_swiglu(const EpiArgs& e, int64_t row, int64_t col, const float (&g)[4],
+                                            const float (&u)[4]) {
+    float gs[4], us[4], hh[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        gs[k] = round_bf(g[k]);
+        us[k] = round_bf(u[k]);
+        hh[k] = swiglu_f(gs[k], us[k]);
+    }
+    const int64_t o = row * e.ld0 + col;
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out0) + o) = pack4(gs);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out1) + o) = pack4(us);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out2) + o) = pack4(hh);
+}
+
 // s_waitcnt vmcnt(N) with the other counters left at their maximum.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -176,24 +260,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         }
     }
 
-    // Accumulator layout of a 32x32 MFMA tile: lane l, element e holds
-    // row (e/4)*8 + (l/32)*4 + e%4, column l%32.
+    // Epilogue on quad-transposed accumulators: this lane owns row
+    // ... + q*8 + (l/32)*4 + l%4 and columns cq..cq+3 of each 32x32 tile.
+    const int jq = lane & 3;
+    const int cq = (lane & 31) & ~3;
 #pragma clang loop unroll(full)
     for (int i = 0; i < 4; ++i) {
 #pragma clang loop unroll(full)
-        for (int e = 0; e < 16; ++e) {
-            const int64_t row = m0 + wm * 128 + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        for (int q = 0; q < 4; ++q) {
+            const int64_t row = m0 + wm * 128 + i * 32 + q * 8 + (lane >> 5) * 4 + jq;
             const bool rok = row < p.M;
+            float w[2][4];
+#pragma clang loop unroll(full)
+            for (int j = 0; j < 2; ++j) {
+                const float v[4] = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
+                quad_transpose(v, w[j], jq);
+            }
             if constexpr (EPI == EPI_SWIGLU) {
                 // a wavefront's 64 B rows are 32 gate rows then 32 up rows of the
                 // same 32 hidden columns
-                const int64_t col = n0 + wn * 32 + (lane & 31);
-                if (rok && col < p.N) epi_swiglu<uint16_t>(p.e, row, col, acc[i][0][e], acc[i][1][e]);
+                const int64_t col = n0 + wn * 32 + cq;
+                if (rok && col < p.N) epi4_swiglu(p.e, row, col, w[0], w[1]);
             } else {
 #pragma clang loop unroll(full)
                 for (int j = 0; j < 2; ++j) {
-                    const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
-                    if (rok && col < p.N) epi_apply<EPI, uint16_t>(p.e, row, col, acc[i][j][e]);
+                    const int64_t col = n0 + wn * 64 + j * 32 + cq;
+                    if (rok && col < p.N) epi4<EPI>(p.e, row, col, w[j]);
                 }
             }
         }
