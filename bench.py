@@ -31,12 +31,38 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FL
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0
 
+# L2-to-memory bytes per launch of each GEMM role at the c3 workload, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs (bytes = 2.0 x FETCH_SIZE KiB + 1.0 x WRITE_SIZE KiB, scales taken from a plain 1 GiB
+# copy kernel measured in the same runs).  Valid only for the GEMM source they were taken on.
+TRAFFIC = {
+    "config": "c3_80layer_p8_stage0",
+    "gemm_source_sha1": "7344008427fd62a17bd5bc8a58c953006e784e6e",
+    "bytes_per_launch": {
+        "gemm_gateup_swiglu": 12.898e9, "gemm_down_residual": 5.907e9, "gemm_dh_swiglu_bwd": 7.771e9,
+        "gemm_dn": 11.809e9, "gemm_wgrad_down": 7.536e9, "gemm_wgrad_gateup": 16.128e9,
+    },
+}
+
+
+def _measured_traffic(config_name, kernel_name):
+    """The counter-measured bytes per launch, or None once the GEMM source has changed since."""
+    import hashlib
+    src = os.path.join(ROOT, "pipeline_schedules_amd", "csrc", "gemm_bf16.hip")
+    try:
+        with open(src, "rb") as f:
+            sha = hashlib.sha1(f.read()).hexdigest()
+    except OSError:
+        return None
+    if sha != TRAFFIC["gemm_source_sha1"] or config_name != TRAFFIC["config"]:
+        return None
+    return TRAFFIC["bytes_per_launch"].get(kernel_name)
+
 
 def _log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(cfg, params_dev, budget_s=15.0):
+def cpu_baseline(cfg, params_dev, budget_s=20.0):
     """Time the float64 oracle (numpy/OpenBLAS, all host cores it is given) on
     one SwiGLU block of this workload's width, forward + backward on a sample
     of tokens sized to take roughly ``budget_s`` seconds."""
@@ -61,7 +87,7 @@ def cpu_baseline(cfg, params_dev, budget_s=15.0):
 
     ts = 64
     dt = run(ts)
-    while dt < budget_s / 4 and ts < 4096:
+    while dt < budget_s / 2 and ts < 8192:
         ts *= 2
         dt = run(ts)
     flops = 18.0 * ts * cfg.d * cfg.f
@@ -89,6 +115,9 @@ def main():
     ap.add_argument("--config", default="c3_80layer_p8_stage0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run a plain fp32 copy kernel (pps_scale by 1.0) three times over this many MiB: "
+                         "a reference of known size for the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one pipeline stage on one GPU; --gpus {args.gpus} is not supported "
@@ -107,6 +136,16 @@ def main():
     stream = torch.cuda.current_stream()
     dtype_id = pps.DTYPE_BY_NAME[cfg.dtype]
     kind_id = pps.KIND_BY_NAME[cfg.kind]
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            pps.scale(dst, src, n, 1.0, pps.DTYPE_FP32, stream)
+        torch.cuda.synchronize()
+        _log(f"copy probe: 3 x {n * 4} bytes read and written")
+        del src, dst
 
     _log(f"workload {cfg.name}: drawing inputs on the device")
     inp = make_device_inputs(cfg, dev)
@@ -181,8 +220,8 @@ def main():
         if dom["flops"]:
             ach = dom["flops"] / (dom["total_ms"] * 1e-3) / 1e12
             roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                        "frac": round(ach / peak, 4), "traffic": None, "kernel": dom["name"],
-                        "avg_launch_ms": dom["total_ms"] / dom["launches"],
+                        "frac": round(ach / peak, 4), "traffic": _measured_traffic(cfg.name, dom["name"]),
+                        "kernel": dom["name"], "avg_launch_ms": dom["total_ms"] / dom["launches"],
                         "flops_per_launch": dom["flops"] / dom["launches"]}
         else:
             ach = dom["bytes"] / (dom["total_ms"] * 1e-3) / 1e9
