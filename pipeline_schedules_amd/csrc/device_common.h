@@ -7,15 +7,19 @@
 namespace pps {
 
 // bf16 <-> fp32.  bf16 is the upper half of an IEEE fp32 word; conversion
-// to bf16 rounds to nearest, ties to even; NaN stays NaN (quiet bit set).
+// to bf16 rounds to nearest, ties to even, and keeps NaN a NaN (gfx950's
+// v_cvt_pk_bf16_f32 does both in one instruction for two values).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-__device__ __forceinline__ uint32_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two fp32 values -> packed bf16 pair (a in the low half).
+__device__ __forceinline__ uint32_t pack2_bf(float a, float b) {
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
+
+__device__ __forceinline__ uint32_t f2bf(float f) { return pack2_bf(f, 0.0f) & 0xffffu; }
 
 // Round an fp32 value to the nearest bf16 value, returned as fp32.
 __device__ __forceinline__ float round_bf(float f) { return bf2f(f2bf(f)); }
@@ -32,7 +36,8 @@ template <> struct Store<float> {
     static __device__ __forceinline__ float round(float v) { return v; }
 };
 
-__device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// sigmoid with the hardware reciprocal (about 1 ulp), not an IEEE divide.
+__device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // h = silu(g) * u with silu(g) = g * sigmoid(g).
 __device__ __forceinline__ float swiglu_f(float g, float u) { return g * sigmoid_f(g) * u; }

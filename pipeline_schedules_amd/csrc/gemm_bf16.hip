@@ -82,28 +82,31 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
 // 0..3, so every global access of the epilogue is an 8-byte (bf16) or 16-byte
 // (fp32) vector and one wavefront access covers 8 rows x 32 columns.
 
-__device__ __forceinline__ float sel4(const float (&v)[4], int i) {
-    return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
-}
-
 template <int CTRL>
 __device__ __forceinline__ float quad_xor(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// v: this lane's 4 rows at its column; w: this lane's row, 4 columns.
-__device__ __forceinline__ void quad_transpose(const float (&v)[4], float (&w)[4], int j) {
-    float r[4];
-    r[0] = sel4(v, j);
-    r[1] = quad_xor<0xB1>(sel4(v, j ^ 1));   // from lane j^1
-    r[2] = quad_xor<0x4E>(sel4(v, j ^ 2));   // from lane j^2
-    r[3] = quad_xor<0x1B>(sel4(v, j ^ 3));   // from lane j^3
-#pragma unroll
-    for (int m = 0; m < 4; ++m) w[m] = sel4(r, m ^ j);
+// 4x4 transpose across a lane quad in two butterfly rounds.  In: lane j holds
+// column j (v[r] = M[r][j]); out: lane j holds row j (w[m] = M[j][m]).  Round
+// one swaps the odd/even elements with lane j^1, round two the element pairs
+// with lane j^2; o1 and o2 are the lane's bits 0 and 1.
+__device__ __forceinline__ void quad_transpose(const float (&v)[4], float (&w)[4], bool o1, bool o2) {
+    float a = o1 ? v[0] : v[1], b = o1 ? v[2] : v[3];
+    a = quad_xor<0xB1>(a);
+    b = quad_xor<0xB1>(b);
+    const float x0 = o1 ? a : v[0], x1 = o1 ? v[1] : a, x2 = o1 ? b : v[2], x3 = o1 ? v[3] : b;
+    float c = o2 ? x0 : x2, d = o2 ? x1 : x3;
+    c = quad_xor<0x4E>(c);
+    d = quad_xor<0x4E>(d);
+    w[0] = o2 ? c : x0;
+    w[1] = o2 ? d : x1;
+    w[2] = o2 ? x2 : c;
+    w[3] = o2 ? x3 : d;
 }
 
 __device__ __forceinline__ uint2 pack4(const float (&w)[4]) {
-    return make_uint2(f2bf(w[0]) | (f2bf(w[1]) << 16), f2bf(w[2]) | (f2bf(w[3]) << 16));
+    return make_uint2(pack2_bf(w[0], w[1]), pack2_bf(w[2], w[3]));
 }
 
 __device__ __forceinline__ void unpack4(uint2 q, float (&w)[4]) {
@@ -111,34 +114,56 @@ __device__ __forceinline__ void unpack4(uint2 q, float (&w)[4]) {
     w[2] = bf2f(q.y & 0xffffu); w[3] = bf2f(q.y >> 16);
 }
 
+// Inputs an epilogue reads for four consecutive output columns.  They are
+// loaded one row group ahead of their use so the loads overlap the math.
+template <int EPI> struct EpiIn {};
+template <> struct EpiIn<EPI_RESID> { uint2 x; };
+template <> struct EpiIn<EPI_SWIGLU_BWD> { uint2 g, u; };
+template <> struct EpiIn<EPI_ACC_F32> { float4 c; };
+
+__device__ __forceinline__ float* acc_ptr(const EpiArgs& e, int64_t row, int64_t col) {
+    return col < e.nsplit ? static_cast<float*>(e.out0) + row * e.ld0 + col
+                          : static_cast<float*>(e.out1) + row * e.ld1 + (col - e.nsplit);
+}
+
+template <int EPI>
+__device__ __forceinline__ void epi_load(const EpiArgs& e, int64_t row, int64_t col, EpiIn<EPI>& in) {
+    if constexpr (EPI == EPI_RESID) {
+        in.x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(e.in0) + row * e.ldi0 + col);
+    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+        in.g = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(e.in0) + row * e.ldi0 + col);
+        in.u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(e.in1) + row * e.ldi0 + col);
+    } else if constexpr (EPI == EPI_ACC_F32) {
+        in.c = *reinterpret_cast<const float4*>(acc_ptr(e, row, col));
+    }
+}
+
 // Four consecutive output columns col..col+3 of one row.
 template <int EPI>
-__device__ __forceinline__ void epi4(const EpiArgs& e, int64_t row, int64_t col, const float (&w)[4]) {
+__device__ __forceinline__ void epi4(const EpiArgs& e, int64_t row, int64_t col, const float (&w)[4],
+                                     const EpiIn<EPI>& in) {
     if constexpr (EPI == EPI_STORE_F32) {
         *reinterpret_cast<float4*>(static_cast<float*>(e.out0) + row * e.ld0 + col) = make_float4(w[0], w[1], w[2], w[3]);
     } else if constexpr (EPI == EPI_STORE) {
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out0) + row * e.ld0 + col) = pack4(w);
     } else if constexpr (EPI == EPI_RESID) {
         float x[4], y[4];
-        unpack4(*reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(e.in0) + row * e.ldi0 + col), x);
+        unpack4(in.x, x);
 #pragma unroll
         for (int k = 0; k < 4; ++k) y[k] = x[k] + w[k];
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out0) + row * e.ld0 + col) = pack4(y);
     } else if constexpr (EPI == EPI_SWIGLU_BWD) {
         float g[4], u[4], dg[4], du[4];
-        unpack4(*reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(e.in0) + row * e.ldi0 + col), g);
-        unpack4(*reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(e.in1) + row * e.ldi0 + col), u);
+        unpack4(in.g, g);
+        unpack4(in.u, u);
 #pragma unroll
         for (int k = 0; k < 4; ++k) swiglu_bwd_f(w[k], g[k], u[k], dg[k], du[k]);
         uint16_t* o = static_cast<uint16_t*>(e.out0) + row * e.ld0;
         *reinterpret_cast<uint2*>(o + col) = pack4(dg);
         *reinterpret_cast<uint2*>(o + e.nsplit + col) = pack4(du);
     } else if constexpr (EPI == EPI_ACC_F32) {
-        float* o = col < e.nsplit ? static_cast<float*>(e.out0) + row * e.ld0 + col
-                                  : static_cast<float*>(e.out1) + row * e.ld1 + (col - e.nsplit);
-        float4 a = *reinterpret_cast<const float4*>(o);
-        a.x += w[0]; a.y += w[1]; a.z += w[2]; a.w += w[3];
-        *reinterpret_cast<float4*>(o) = a;
+        const float4 c = in.c;
+        *reinterpret_cast<float4*>(acc_ptr(e, row, col)) = make_float4(c.x + w[0], c.y + w[1], c.z + w[2], c.w + w[3]);
     }
 }
 
@@ -146,16 +171,15 @@ __device__ __forceinline__ void epi4(const EpiArgs& e, int64_t row, int64_t col,
 // h = silu(g) u computed from the stored values.
 __device__ __forceinline__ void epi4_swiglu(const EpiArgs& e, int64_t row, int64_t col, const float (&g)[4],
                                             const float (&u)[4]) {
+    const uint2 gp = pack4(g), up = pack4(u);
     float gs[4], us[4], hh[4];
+    unpack4(gp, gs);
+    unpack4(up, us);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        gs[k] = round_bf(g[k]);
-        us[k] = round_bf(u[k]);
-        hh[k] = swiglu_f(gs[k], us[k]);
-    }
+    for (int k = 0; k < 4; ++k) hh[k] = swiglu_f(gs[k], us[k]);
     const int64_t o = row * e.ld0 + col;
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out0) + o) = pack4(gs);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out1) + o) = pack4(us);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out0) + o) = gp;
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out1) + o) = up;
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out2) + o) = pack4(hh);
 }
 
@@ -238,43 +262,68 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    if (nk > 0) {
-        issue(0);
-        wait_vm<0>();
-        __syncthreads();
-        bf16x8 fa[2][4], fb[2][2];
-        for (int kt = 0; kt < nk; ++kt) {
-            if (kt + 1 < nk) issue(kt + 1);   // into the other stage, freed by the last barrier
-            frags(kt, 0, fa[0], fb[0]);
-#pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk) {
-                if (kk + 1 < BK / 16) frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
-            }
-            wait_vm<0>();
-            __syncthreads();
-        }
-    }
-
     // Epilogue on quad-transposed accumulators: this lane owns row
     // ... + q*8 + (l/32)*4 + l%4 and columns cq..cq+3 of each 32x32 tile.
     const int jq = lane & 3;
     const int cq = (lane & 31) & ~3;
+    const int64_t rbase = m0 + wm * 128 + (lane >> 5) * 4 + jq;
+    constexpr int PD = EPI == EPI_RESID ? 2 : 1;   // row groups loaded ahead (registers allow)
+    EpiIn<EPI> in[PD + 1][4][2];
+    auto prefetch = [&](int i, EpiIn<EPI> (&dst)[4][2]) {
+        if constexpr (EPI == EPI_RESID || EPI == EPI_SWIGLU_BWD || EPI == EPI_ACC_F32) {
+#pragma clang loop unroll(full)
+            for (int q = 0; q < 4; ++q) {
+                const int64_t row = rbase + i * 32 + q * 8;
+#pragma clang loop unroll(full)
+                for (int j = 0; j < 2; ++j) {
+                    const int64_t col = n0 + wn * 64 + j * 32 + cq;
+                    if (row < p.M && col < p.N) epi_load<EPI>(p.e, row, col, dst[q][j]);
+                }
+            }
+        }
+    };
+    bf16x8 fa[2][4], fb[2][2];
+    auto kstep = [&](int kt, bool last) {
+        if (!last) issue(kt + 1);   // into the other stage, freed by the last barrier
+        frags(kt, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            if (kk + 1 < BK / 16) frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
+        }
+        if (!last) {
+            wait_vm<0>();
+            __syncthreads();
+        }
+    };
+    if (nk > 0) {
+        issue(0);
+        wait_vm<0>();
+        __syncthreads();
+        for (int kt = 0; kt < nk - 1; ++kt) kstep(kt, false);
+    }
+    // the epilogue's first inputs load under the last K step's MFMAs
+#pragma clang loop unroll(full)
+    for (int i = 0; i < PD; ++i) prefetch(i, in[i]);
+    if (nk > 0) kstep(nk - 1, true);
+
+
 #pragma clang loop unroll(full)
     for (int i = 0; i < 4; ++i) {
+        if (i + PD < 4) prefetch(i + PD, in[(i + PD) % (PD + 1)]);
 #pragma clang loop unroll(full)
         for (int q = 0; q < 4; ++q) {
-            const int64_t row = m0 + wm * 128 + i * 32 + q * 8 + (lane >> 5) * 4 + jq;
+            const int64_t row = rbase + i * 32 + q * 8;
             const bool rok = row < p.M;
             float w[2][4];
 #pragma clang loop unroll(full)
             for (int j = 0; j < 2; ++j) {
                 const float v[4] = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
-                quad_transpose(v, w[j], jq);
+                quad_transpose(v, w[j], (jq & 1) != 0, (jq & 2) != 0);
             }
             if constexpr (EPI == EPI_SWIGLU) {
                 // a wavefront's 64 B rows are 32 gate rows then 32 up rows of the
@@ -285,7 +334,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
 #pragma clang loop unroll(full)
                 for (int j = 0; j < 2; ++j) {
                     const int64_t col = n0 + wn * 64 + j * 32 + cq;
-                    if (rok && col < p.N) epi4<EPI>(p.e, row, col, w[j]);
+                    if (rok && col < p.N) epi4<EPI>(p.e, row, col, w[j], in[i % (PD + 1)][q][j]);
                 }
             }
         }
