@@ -8,13 +8,13 @@
 //
 // Tiling: macro-tile 256 x 256 x 64, 512 threads = 8 wavefronts in a 2 x 4
 // grid, 128 x 64 per wavefront = 4 x 2 tiles of v_mfma_f32_32x32x16_bf16
-// (128 fp32 accumulators per lane, two wavefronts per SIMD).  Eight
-// wavefronts per CU are needed to pull operands from L2 fast enough: with
-// four, a CU sustains about half the bytes per clock the matrix cores
-// consume at this tile size.
+// (128 fp32 accumulators per lane, two wavefronts per SIMD).
 //
-// Data path: global -> LDS by direct-to-LDS buffer loads (no VGPR staging),
-// two 64 KB stages (A and B tiles of 256 rows x 128 bytes), one barrier per
+// Data path: every operand tile is requested two K steps before it is
+// multiplied, and the requests are spread over the MFMAs of the step (a
+// stalled load issue then never idles the matrix core).  A goes straight to
+// LDS (direct-to-LDS buffer loads) into three 32 KB slots; B goes through two
+// register sets into two 32 KB slots (160 KB of LDS in all).  One barrier per
 // K step; MFMA operands are read with ds_read_b128.  In LDS, 16-byte chunk c
 // of row r sits at position c ^ ((r >> 1) & 7), which keeps the 16 lanes of
 // every ds_read_b128 phase on distinct banks (64 banks, two 128-byte rows
@@ -35,11 +35,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 512, NSTAGE = 2;
+constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 512;
 constexpr int ROWB = BK * 2;             // 128 bytes per LDS row
 constexpr int OPB = 256 * ROWB;          // 32 KB per operand tile
-constexpr int STAGEB = 2 * OPB;          // A + B
-constexpr int LDS_BYTES = NSTAGE * STAGEB;
+constexpr int ASLOTS = 3, BSLOTS = 2;    // LDS slots of A (direct loads) and B (from registers)
+constexpr int BBASE = ASLOTS * OPB;
+constexpr int LDS_BYTES = (ASLOTS + BSLOTS) * OPB;   // 160 KB
 constexpr int GROUP_M = 8;
 constexpr uint32_t OOB = 0x80000000u;    // an offset past every operand extent
 
@@ -183,10 +184,10 @@ __device__ __forceinline__ void epi4_swiglu(const EpiArgs& e, int64_t row, int64
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out2) + o) = pack4(hh);
 }
 
-// s_waitcnt vmcnt(N) with the other counters left at their maximum.
+// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt left at its maximum).
 template <int N>
-__device__ __forceinline__ void wait_vm() {
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
 template <int EPI>
@@ -201,57 +202,73 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     const int64_t n0 = (int64_t)tn * (p.swiglu ? BN / 2 : BN);   // first output column
     const int64_t nb0 = (int64_t)tn * BN;                         // first B row
 
-    // Loader: per K step each wavefront issues 4 A and 4 B direct-to-LDS loads;
-    // load q fills LDS rows (wave*4+q)*8 .. +7 (1 KB); lane l covers row + l/8,
-    // LDS chunk l&7, i.e. logical chunk (l&7) ^ ((row>>1)&7).
+    // Loader: per K step each wavefront moves 4 A and 4 B pieces of 1 KB; piece
+    // q holds LDS rows (wave*4+q)*8 .. +7; lane l covers row + l/8 and LDS chunk
+    // l&7, i.e. logical chunk lcq[q] = (l&7) ^ ((row>>1)&7).  The per-lane byte
+    // offsets stay fixed within a K segment; the K step rides in soffset.
     const int lrow = lane >> 3;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     int lcq[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) lcq[q] = (lane & 7) ^ (((wave * 4 + q) * 4 + (lane >> 4)) & 7);
-    uint32_t aoff[2][4], boff[2][4];
-    rsrc_t ar[2], br[2];
-    int nkt[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const Seg& g = p.seg[s < p.nseg ? s : 0];
-        ar[s] = make_rsrc(g.A, g.a_bytes);
-        br[s] = make_rsrc(g.B, g.b_bytes);
-        nkt[s] = s < p.nseg ? (int)((g.K + BK - 1) / BK) : 0;
+    uint32_t aoff[4], boff[4];
+    rsrc_t ar, br;
+    int64_t K = 0;
+    auto set_seg = [&](int s) {
+        const Seg& g = p.seg[s];
+        ar = make_rsrc(g.A, g.a_bytes);
+        br = make_rsrc(g.B, g.b_bytes);
+        K = g.K;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int row = (wave * 4 + q) * 8 + lrow;
             const int64_t ra = m0 + row, rb = nb0 + row;
-            aoff[s][q] = ra < p.M ? (uint32_t)(ra * g.lda * 2 + lcq[q] * 16) : OOB;
-            boff[s][q] = rb < p.NB ? (uint32_t)(rb * g.ldb * 2 + lcq[q] * 16) : OOB;
+            aoff[q] = ra < p.M ? (uint32_t)(ra * g.lda * 2 + lcq[q] * 16) : OOB;
+            boff[q] = rb < p.NB ? (uint32_t)(rb * g.ldb * 2 + lcq[q] * 16) : OOB;
         }
-    }
-    const int nk = nkt[0] + nkt[1];
-
-    auto issue = [&](int kt) {
-        const int s = kt < nkt[0] ? 0 : 1;
-        const int64_t k0 = (int64_t)(kt - (s ? nkt[0] : 0)) * BK;
-        char* st = smem + (kt % NSTAGE) * STAGEB;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const bool kv = k0 + lcq[q] * 8 < p.seg[s].K;
-            const uint32_t ao = (kv && aoff[s][q] != OOB) ? aoff[s][q] + (uint32_t)(k0 * 2) : OOB;
-            const uint32_t bo = (kv && boff[s][q] != OOB) ? boff[s][q] + (uint32_t)(k0 * 2) : OOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(s ? ar[1] : ar[0], (LDS_AS void*)(st + (wave * 4 + q) * 1024), 16, ao, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(s ? br[1] : br[0], (LDS_AS void*)(st + OPB + (wave * 4 + q) * 1024), 16, bo, 0, 0, 0);
-        }
+    };
+    // Piece q of K tile kt (past the segment's K: zeros).  Branch-free, so the
+    // compiler's wait counts for the B registers stay exact across the loop.
+    auto chunks_left = [&](int kt) {
+        const int64_t rem = K - (int64_t)kt * BK;
+        return rem <= 0 ? 0 : rem >= BK ? BK / 8 : (int)rem / 8;   // valid 16-byte chunks per row
+    };
+    auto issueA = [&](int kt, int q) {
+        char* st = smem + (kt % ASLOTS) * OPB;
+        const uint32_t ao = lcq[q] < chunks_left(kt) ? aoff[q] : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (LDS_AS void*)(st + (wave_s * 4 + q) * 1024), 16, ao,
+                                                 (uint32_t)kt * (BK * 2), 0, 0);
+    };
+    auto issueB = [&](int kt, int q, uint4 (&rb)[4]) {
+        const uint32_t bo = lcq[q] < chunks_left(kt) ? boff[q] : OOB;
+        auto v = __builtin_amdgcn_raw_buffer_load_b128(br, bo, (uint32_t)kt * (BK * 2), 0);
+        rb[q] = *reinterpret_cast<uint4*>(&v);
+    };
+    // B pieces reach LDS through inline stores, so the compiler does not make
+    // them wait for the in-flight direct A loads (which target other slots).
+    const uint32_t bl0 = (uint32_t)(uintptr_t)(smem + BBASE + (wave * 4) * 1024 + lane * 16);
+    auto bstore = [&](int kt, const uint4 (&rb)[4]) {
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        const uint32_t a = bl0 + (uint32_t)((kt & 1) * OPB);
+        asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:1024\n\t"
+                     "ds_write_b128 %0, %3 offset:2048\n\tds_write_b128 %0, %4 offset:3072"
+                     :: "v"(a), "v"(__builtin_bit_cast(u32x4, rb[0])), "v"(__builtin_bit_cast(u32x4, rb[1])),
+                        "v"(__builtin_bit_cast(u32x4, rb[2])), "v"(__builtin_bit_cast(u32x4, rb[3]))
+                     : "memory");
     };
 
     // MFMA operand fragment: row r, logical chunk ch at r*128 + (ch ^ ((r>>1)&7))*16.
     const int fsw = ((lane & 31) >> 1) & 7;
     auto frags = [&](int kt, int kk, bf16x8 (&a)[4], bf16x8 (&b)[2]) {
-        const char* st = smem + (kt % NSTAGE) * STAGEB;
+        const char* sa = smem + (kt % ASLOTS) * OPB;
+        const char* sb = smem + BBASE + (kt & 1) * OPB;
         const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) << 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            a[i] = *reinterpret_cast<const bf16x8*>(st + (wm * 128 + i * 32 + (lane & 31)) * ROWB + pc);
+            a[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32 + (lane & 31)) * ROWB + pc);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            b[j] = *reinterpret_cast<const bf16x8*>(st + OPB + (wn * 64 + j * 32 + (lane & 31)) * ROWB + pc);
+            b[j] = *reinterpret_cast<const bf16x8*>(sb + (wn * 64 + j * 32 + (lane & 31)) * ROWB + pc);
     };
 
     f32x16 acc[4][2];
@@ -261,6 +278,31 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // One K step: multiply tile kt while tile kt+2 is requested (its A pieces
+    // into LDS slot (kt+2)%3, its B pieces into rfill, which held tile kt);
+    // then store tile kt+1's B (in rnext since the previous step) and barrier.
+    auto step = [&](int kt, uint4 (&rnext)[4], uint4 (&rfill)[4]) {
+        bf16x8 fa[2][4], fb[2][2];
+        frags(kt, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            issueA(kt + 2, kk);
+            issueB(kt + 2, kk, rfill);
+            if (kk + 1 < BK / 16) frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
+        }
+        bstore(kt + 1, rnext);   // the compiler waits for rnext's loads first
+        // vmcnt(8): everything but this step's 8 loads has landed, i.e. tile
+        // kt+1's A pieces; lgkmcnt(0): the B stores and this step's reads are
+        // done.  A bare barrier: a fence would also wait for tile kt+2.
+        wait_vm_lgkm0<8>();
+        __builtin_amdgcn_s_barrier();
+    };
 
     // Epilogue on quad-transposed accumulators: this lane owns row
     // ... + q*8 + (l/32)*4 + l%4 and columns cq..cq+3 of each 32x32 tile.
@@ -282,34 +324,35 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
             }
         }
     };
-    bf16x8 fa[2][4], fb[2][2];
-    auto kstep = [&](int kt, bool last) {
-        if (!last) issue(kt + 1);   // into the other stage, freed by the last barrier
-        frags(kt, 0, fa[0], fb[0]);
+
+    uint4 rB[2][4];
+    for (int s = 0; s < p.nseg; ++s) {
+        set_seg(s);
+        const int nk = (int)((K + BK - 1) / BK);
+        if (nk == 0) continue;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            if (kk + 1 < BK / 16) frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int q = 0; q < 4; ++q) issueA(t2, q);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
+            for (int q = 0; q < 4; ++q) issueB(t2, q, rB[t2]);
         }
-        if (!last) {
-            wait_vm<0>();
-            __syncthreads();
+        bstore(0, rB[0]);
+        wait_vm_lgkm0<8>();   // tile 0 complete (A in LDS, B stored)
+        __builtin_amdgcn_s_barrier();
+        const int nk2 = (nk + 1) & ~1;   // an odd count runs one all-zero tile
+        for (int kt = 0; kt < nk2; kt += 2) {
+            step(kt, rB[1], rB[0]);
+            step(kt + 1, rB[0], rB[1]);
         }
-    };
-    if (nk > 0) {
-        issue(0);
-        wait_vm<0>();
-        __syncthreads();
-        for (int kt = 0; kt < nk - 1; ++kt) kstep(kt, false);
+        // the last steps requested two all-zero tiles past K: let them land
+        // before another segment reuses the slots (and before the epilogue)
+        wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
     }
-    // the epilogue's first inputs load under the last K step's MFMAs
 #pragma clang loop unroll(full)
     for (int i = 0; i < PD; ++i) prefetch(i, in[i]);
-    if (nk > 0) kstep(nk - 1, true);
+
 
 
 #pragma clang loop unroll(full)
