@@ -36,10 +36,10 @@ PEAK_HBM_GBS = 8000.0
 # copy kernel measured in the same runs).  Valid only for the GEMM source they were taken on.
 TRAFFIC = {
     "config": "c3_80layer_p8_stage0",
-    "gemm_source_sha1": "7344008427fd62a17bd5bc8a58c953006e784e6e",
+    "gemm_source_sha1": "3bc789463e6c4fee37eb04d71914a40f6d44a8e5",
     "bytes_per_launch": {
-        "gemm_gateup_swiglu": 12.898e9, "gemm_down_residual": 5.907e9, "gemm_dh_swiglu_bwd": 7.771e9,
-        "gemm_dn": 11.809e9, "gemm_wgrad_down": 7.536e9, "gemm_wgrad_gateup": 16.128e9,
+        "gemm_gateup_swiglu": 15.600e9, "gemm_down_residual": 5.906e9, "gemm_dh_swiglu_bwd": 8.031e9,
+        "gemm_dn": 11.560e9, "gemm_wgrad_down": 7.521e9, "gemm_wgrad_gateup": 15.680e9,
     },
 }
 

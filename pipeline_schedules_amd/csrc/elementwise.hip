@@ -147,13 +147,26 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
     }
 }
 
+// out[j] += sum_w partial[w, j] in a fixed order: thread (c, g) of a workgroup
+// sums rows g, g+8, g+16, ... of column j = 32*block + c, then the 8 partial
+// sums are added in g order.  32 columns per workgroup: d/32 workgroups fill
+// the chip where one thread per column would leave most CUs idle.
 __global__ __launch_bounds__(256) void column_reduce_kernel(const float* __restrict__ partial, int rows, int64_t d,
                                                             float* __restrict__ out) {
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (j >= d) return;
+    __shared__ float part[8][33];
+    const int c = threadIdx.x & 31, g = threadIdx.x >> 5;
+    const int64_t j = (int64_t)blockIdx.x * 32 + c;
     float s = 0.0f;
-    for (int w = 0; w < rows; ++w) s += partial[(int64_t)w * d + j];
-    out[j] += s;
+    if (j < d)
+        for (int w = g; w < rows; w += 8) s += partial[(int64_t)w * d + j];
+    part[g][c] = s;
+    __syncthreads();
+    if (g == 0 && j < d) {
+        float t = part[0][c];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) t += part[k][c];
+        out[j] += t;
+    }
 }
 
 // chunks [0, nx) recompute n = (x r) gamma on [T,d]; chunks [nx, nx+nh)
@@ -328,7 +341,7 @@ hipError_t rmsnorm_bwd(int dtype, const float* dn, const void* x, const float* r
 
 hipError_t column_reduce_acc(const float* partial, int rows, int64_t d, float* out, hipStream_t s) {
     if (rows <= 0 || d <= 0) return hipSuccess;
-    hipLaunchKernelGGL(column_reduce_kernel, dim3(grid_for(d)), dim3(256), 0, s, partial, rows, d, out);
+    hipLaunchKernelGGL(column_reduce_kernel, dim3((unsigned)((d + 31) / 32)), dim3(256), 0, s, partial, rows, d, out);
     return hipGetLastError();
 }
 
