@@ -290,6 +290,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
             issueA(kt + 2, kk);
             issueB(kt + 2, kk, rfill);
             if (kk + 1 < BK / 16) frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+            // keep the next sub-step's fragment reads ahead of this sub-step's
+            // MFMAs (left alone, the scheduler sinks them to their use)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
