@@ -230,6 +230,25 @@ def main():
                         "avg_launch_ms": dom["total_ms"] / dom["launches"],
                         "bytes_per_launch": dom["bytes"] / dom["launches"]}
 
+    # The P-stage timeline this stage's measured per-op times imply (no
+    # transfer time): every stage is assumed to cost what this one does.
+    pipeline_model = None
+    if kernels and cfg.block == "swiglu" and cfg.v == 1:
+        per_mb = lambda names: sum(kernels[n]["total_ms_per_step"] for n in names if n in kernels) / cfg.M
+        t_f = per_mb(["rmsnorm_fwd", "gemm_gateup_swiglu", "gemm_down_residual"])
+        t_bx = per_mb(["gemm_dh_swiglu_bwd", "gemm_dn", "rmsnorm_bwd_residual", "dgamma_reduce"])
+        # "copy" also holds the once-per-pass weight refresh; it is charged to W
+        t_w = per_mb(["prep_w", "gemm_wgrad_down", "gemm_wgrad_gateup", "copy"])
+        pipeline_model = {"P": cfg.P, "M": cfg.M, "t_f_ms": round(t_f, 3), "t_b_ms": round(t_bx + t_w, 3),
+                          "t_b_input_ms": round(t_bx, 3), "t_w_ms": round(t_w, 3), "transfer_ms": 0.0}
+        for name, kind, v, tf, tb, tw in (("gpipe", pps.GPIPE, 1, t_f, t_bx + t_w, 0.0),
+                                          ("1f1b", pps.ONE_F_ONE_B, 1, t_f, t_bx + t_w, 0.0),
+                                          ("interleaved_v2", pps.ONE_F_ONE_B, 2, t_f / 2, (t_bx + t_w) / 2, 0.0),
+                                          ("zb1p", pps.ZB1P, 1, t_f, t_bx, t_w),
+                                          ("zb2p", pps.ZB2P, 1, t_f, t_bx, t_w)):
+            mk, bubble = pps.simulate_pipeline(cfg.P, cfg.M, v, kind, tf, tb, tw)
+            pipeline_model[name] = {"step_ms": round(mk, 1), "bubble": round(bubble, 4)}
+
     cpu = None
     if not args.no_cpu_baseline and cfg.block == "swiglu":
         _log("cpu baseline: float64 oracle on a token sample")
@@ -261,6 +280,7 @@ def main():
         "flops_per_step": flops_per_pass,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "pipeline_model": pipeline_model,
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)

@@ -98,6 +98,27 @@ typedef struct pps_op {
 int pps_make_schedule(int P, int M, int k, int v, int kind,
                       pps_op* ops, int cap, int* n_ops);
 
+/*
+ * pps_simulate_pipeline -- predicted timeline of all P stages running one
+ * schedule kind with given per-op durations (any time unit).
+ *
+ * Host only, pure.  Each device runs its op list (as pps_make_schedule builds
+ * it for that stage; the ZB kinds keep their unit-cost W placement) in order,
+ * each op as soon as the device is free and its dependencies have ended
+ * ([Sched §08]: an op waits for its device's previous op and for the results
+ * it needs; [1F1B §4.3], [Sched §04]: the idle share of that timeline is the
+ * bubble).  Durations: t_f = forward of one micro-batch (per chunk when
+ * v > 1); t_b = its backward, including the weight gradient unless the kind
+ * is split; t_w = the deferred weight-gradient op (ZB kinds; otherwise
+ * unused).  Transfers between stages take no time.
+ * Out: *makespan = end of the last op; *bubble = 1 - (busy time summed over
+ * the P devices) / (P * makespan).
+ * Returns PPS_OK; PPS_EINVAL for the shapes pps_make_schedule rejects, a
+ * negative or non-finite duration, or a NULL output.
+ */
+int pps_simulate_pipeline(int P, int M, int v, int kind, double t_f, double t_b, double t_w,
+                          double* makespan, double* bubble);
+
 /* ---- stage handle -------------------------------------------------------- */
 #define PPS_BLOCK_SWIGLU   0  /* RMSNorm -> gate/up -> SiLU-gate -> down -> +x   */
 #define PPS_BLOCK_TOY_GELU 1  /* Linear(d->d) with bias, then exact GELU (fp32) */

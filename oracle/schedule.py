@@ -369,6 +369,55 @@ def timeline(lists, starts):
     return rows
 
 
+def simulate_timed(lists, durations, v=1):
+    """The same in-order ASAP execution with per-op durations: an op starts
+    when its device's previous op has ended and its dependencies have ended
+    ([Sched §08]).  ``durations`` maps op kind (F, B, W) to its duration.
+
+    Returns (makespan, bubble) with bubble = 1 - busy / (P * makespan), the
+    idle share of the P device timelines ([1F1B §4.3], [Sched §04]).
+    """
+    P = len(lists)
+    end = {}
+    ptr = [0] * P
+    free_at = [0.0] * P
+    busy = 0.0
+    makespan = 0.0
+    remaining = sum(len(o) for o in lists)
+    while remaining:
+        progressed = False
+        for k in range(P):
+            while ptr[k] < len(lists[k]):
+                op = lists[k][ptr[k]]
+                deps = _deps(op, k, P, v)
+                if any(d not in end for d in deps):
+                    break
+                t = max([free_at[k]] + [end[d] for d in deps])
+                dur = float(durations[op[0]])
+                end[(op[0], k, op[1], op[2])] = t + dur
+                free_at[k] = t + dur
+                busy += dur
+                makespan = max(makespan, t + dur)
+                ptr[k] += 1
+                remaining -= 1
+                progressed = True
+        if not progressed:
+            raise Deadlock("no device can progress")
+    return makespan, (1.0 - busy / (P * makespan) if makespan > 0 else 0.0)
+
+
+def all_stage_lists(P, M, v=1, kind=ONE_F_ONE_B):
+    """Op lists (op, mb, chunk) of all P devices as the schedule runs them
+    (ZB kinds: with their unit-cost W placement)."""
+    if kind in (ZB1P, ZB2P):
+        return simulate_zb(P, M, 1 if kind == ZB1P else 2)[0]
+    if kind == GPIPE:
+        return [gpipe(P, M, k) for k in range(P)]
+    if v > 1:
+        return [interleaved(P, M, k, v) for k in range(P)]
+    return [one_f_one_b(P, M, k) for k in range(P)]
+
+
 def total_time(starts):
     return max((t + 1 for st in starts for t in st), default=0)
 

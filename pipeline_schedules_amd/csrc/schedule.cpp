@@ -14,6 +14,7 @@
 #include "schedule_internal.h"
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <deque>
 
@@ -73,31 +74,38 @@ void list_interleaved(int P, int M, int k, int v, std::vector<Op3>& out) {
 
 // ---- unit-cost execution ----------------------------------------------------
 
-struct EndTimes {
+// End time of every F and B op, per virtual stage and micro-batch; T is int
+// for the unit-cost placement and double for timed simulation.  -1 = not yet
+// ended.
+template <typename T>
+struct EndTimesT {
     int P, M, v;
-    std::vector<int> f, b;   // [virtual stage][mb], -1 = not yet ended
-    EndTimes(int P_, int M_, int v_) : P(P_), M(M_), v(v_),
-        f((size_t)P_ * v_ * M_, -1), b((size_t)P_ * v_ * M_, -1) {}
-    int& F(int vs, int mb) { return f[(size_t)vs * M + mb]; }
-    int& B(int vs, int mb) { return b[(size_t)vs * M + mb]; }
+    std::vector<T> f, b;
+    EndTimesT(int P_, int M_, int v_) : P(P_), M(M_), v(v_),
+        f((size_t)P_ * v_ * M_, T(-1)), b((size_t)P_ * v_ * M_, T(-1)) {}
+    T& F(int vs, int mb) { return f[(size_t)vs * M + mb]; }
+    T& B(int vs, int mb) { return b[(size_t)vs * M + mb]; }
 };
+using EndTimes = EndTimesT<int>;
 
 // Earliest start of `op` on device `dev` given the ended ops, or -1 if a
 // dependency has not ended.  Forward needs the previous virtual stage's
 // forward; backward needs its own forward and the next virtual stage's
 // backward; W needs its own backward.
-int ready_time(EndTimes& e, const Op3& op, int dev) {
+template <typename T>
+T ready_time(EndTimesT<T>& e, const Op3& op, int dev) {
     const int vs = op.chunk * e.P + dev;
     const int last = e.P * e.v - 1;
-    if (op.kind == OP_F) return vs > 0 ? e.F(vs - 1, op.mb) : 0;
+    if (op.kind == OP_F) return vs > 0 ? e.F(vs - 1, op.mb) : T(0);
     if (op.kind == OP_W) return e.B(vs, op.mb);
-    const int own = e.F(vs, op.mb);
+    const T own = e.F(vs, op.mb);
     if (own < 0 || vs == last) return own;
-    const int down = e.B(vs + 1, op.mb);
-    return down < 0 ? -1 : std::max(own, down);
+    const T down = e.B(vs + 1, op.mb);
+    return down < 0 ? T(-1) : std::max(own, down);
 }
 
-void mark_end(EndTimes& e, const Op3& op, int dev, int end) {
+template <typename T>
+void mark_end(EndTimesT<T>& e, const Op3& op, int dev, T end) {
     const int vs = op.chunk * e.P + dev;
     if (op.kind == OP_F) e.F(vs, op.mb) = end;
     else if (op.kind == OP_B) e.B(vs, op.mb) = end;
@@ -123,6 +131,40 @@ bool run_fixed(const std::vector<std::vector<Op3>>& lists, int P, int M, int v,
                 start[d].push_back(t);
                 mark_end(e, op, d, t + 1);
                 free_at[d] = t + 1;
+                ++pos[d];
+                --left;
+                moved = true;
+            }
+        }
+        if (!moved) return false;
+    }
+    return true;
+}
+
+// The same in-order ASAP execution with per-op durations (F, B, W).  Returns
+// false on deadlock.
+bool run_timed(const std::vector<std::vector<Op3>>& lists, int P, int M, int v, const double (&dur)[3],
+               double& makespan, double& busy) {
+    EndTimesT<double> e(P, M, v);
+    std::vector<size_t> pos(P, 0);
+    std::vector<double> free_at(P, 0.0);
+    size_t left = 0;
+    for (int d = 0; d < P; ++d) left += lists[d].size();
+    makespan = 0.0;
+    busy = 0.0;
+    while (left) {
+        bool moved = false;
+        for (int d = 0; d < P; ++d) {
+            while (pos[d] < lists[d].size()) {
+                const Op3& op = lists[d][pos[d]];
+                const double r = ready_time(e, op, d);
+                if (r < 0) break;
+                const double t = std::max(r, free_at[d]);
+                const double end = t + dur[op.kind];
+                mark_end(e, op, d, end);
+                free_at[d] = end;
+                busy += dur[op.kind];
+                makespan = std::max(makespan, end);
                 ++pos[d];
                 --left;
                 moved = true;
@@ -190,16 +232,18 @@ bool run_zb(int P, int M, int budget_scale, std::vector<std::vector<Op3>>& lists
 
 }  // namespace
 
-int build_schedule(int P, int M, int k, int v, int kind, std::vector<pps_op>& out) {
-    out.clear();
-    if (P < 1 || M < 1 || v < 1 || k < 0 || k >= P) return PPS_EINVAL;
+namespace {
+
+// Op lists of all P devices for a schedule kind, with their unit-cost start
+// times.  Returns a PPS_* status.
+int build_lists(int P, int M, int v, int kind, std::vector<std::vector<Op3>>& lists,
+                std::vector<std::vector<int>>& start, bool& split) {
+    if (P < 1 || M < 1 || v < 1) return PPS_EINVAL;
     if (kind < PPS_GPIPE || kind > PPS_ZB2P) return PPS_EINVAL;
     if ((long long)P * v * M > (1LL << 24)) return PPS_EINVAL;
     if (v > 1 && (kind != PPS_1F1B || M % P != 0)) return PPS_EINVAL;
-
-    std::vector<std::vector<Op3>> lists(P);
-    std::vector<std::vector<int>> start;
-    bool split = false;
+    lists.assign(P, {});
+    split = false;
     if (kind == PPS_ZB1P || kind == PPS_ZB2P) {
         if (!run_zb(P, M, kind == PPS_ZB1P ? 1 : 2, lists, start)) return PPS_EINVAL;
         split = true;
@@ -211,6 +255,19 @@ int build_schedule(int P, int M, int k, int v, int kind, std::vector<pps_op>& ou
         }
         if (!run_fixed(lists, P, M, v, start)) return PPS_EINVAL;
     }
+    return PPS_OK;
+}
+
+}  // namespace
+
+int build_schedule(int P, int M, int k, int v, int kind, std::vector<pps_op>& out) {
+    out.clear();
+    if (k < 0 || k >= P) return PPS_EINVAL;
+    std::vector<std::vector<Op3>> lists;
+    std::vector<std::vector<int>> start;
+    bool split = false;
+    const int rc = build_lists(P, M, v, kind, lists, start, split);
+    if (rc != PPS_OK) return rc;
 
     // Stash slots of device k: lowest free index, taken at F, released at B
     // (at W when split).
@@ -259,5 +316,23 @@ extern "C" int pps_make_schedule(int P, int M, int k, int v, int kind,
     *n_ops = (int)list.size();
     if (cap < (int)list.size()) return PPS_EFULL;
     std::memcpy(ops, list.data(), list.size() * sizeof(pps_op));
+    return PPS_OK;
+}
+
+extern "C" int pps_simulate_pipeline(int P, int M, int v, int kind, double t_f, double t_b, double t_w,
+                                     double* makespan, double* bubble) {
+    if (!makespan || !bubble) return PPS_EINVAL;
+    for (double t : {t_f, t_b, t_w})
+        if (!(t >= 0.0) || !std::isfinite(t)) return PPS_EINVAL;
+    std::vector<std::vector<pps::Op3>> lists;
+    std::vector<std::vector<int>> start;
+    bool split = false;
+    const int rc = pps::build_lists(P, M, v, kind, lists, start, split);
+    if (rc != PPS_OK) return rc;
+    const double dur[3] = {t_f, t_b, t_w};
+    double end = 0.0, busy = 0.0;
+    if (!pps::run_timed(lists, P, M, v, dur, end, busy)) return PPS_EINVAL;
+    *makespan = end;
+    *bubble = end > 0.0 ? 1.0 - busy / ((double)P * end) : 0.0;
     return PPS_OK;
 }

@@ -32,7 +32,7 @@ EXPORTED = [
     "pps_make_schedule", "pps_stage_create", "pps_stage_forward", "pps_stage_backward",
     "pps_stage_backward_weight", "pps_stage_zero_grad", "pps_stage_get_grad", "pps_stage_sync",
     "pps_stage_get_stats", "pps_stage_get_oplog", "pps_stage_kernel_times", "pps_kernel_name",
-    "pps_stage_destroy", "pps_strerror", "pps_scale",
+    "pps_stage_destroy", "pps_strerror", "pps_scale", "pps_simulate_pipeline",
 ]
 
 
@@ -103,6 +103,8 @@ def lib():
         L.pps_strerror.argtypes = [i32]
         L.pps_strerror.restype = ctypes.c_char_p
         L.pps_scale.argtypes = [vp, vp, i64, ctypes.c_float, i32, vp]
+        dbl = ctypes.c_double
+        L.pps_simulate_pipeline.argtypes = [i32, i32, i32, i32, dbl, dbl, dbl, ctypes.POINTER(dbl), ctypes.POINTER(dbl)]
         for name in EXPORTED:
             if name not in ("pps_kernel_name", "pps_stage_destroy", "pps_strerror"):
                 getattr(L, name).restype = ctypes.c_int
@@ -132,6 +134,16 @@ def make_schedule(P, M, k, v=1, kind=ONE_F_ONE_B):
     arr = (PpsOp * max(n.value, 1))()
     _check(lib().pps_make_schedule(P, M, k, v, kind, arr, n.value, ctypes.byref(n)), "pps_make_schedule")
     return [arr[i].as_tuple() for i in range(n.value)]
+
+
+def simulate_pipeline(P, M, v, kind, t_f, t_b, t_w=0.0):
+    """(makespan, bubble) of all P stages running ``kind`` with per-op
+    durations t_f, t_b (and t_w for the ZB kinds)."""
+    mk = ctypes.c_double(0.0)
+    bu = ctypes.c_double(0.0)
+    _check(lib().pps_simulate_pipeline(P, M, v, kind, float(t_f), float(t_b), float(t_w), ctypes.byref(mk),
+                                       ctypes.byref(bu)), "pps_simulate_pipeline")
+    return mk.value, bu.value
 
 
 def scale(dst, src, n, factor, dtype, stream=None):

@@ -3,6 +3,7 @@ declared entry point, the schedule generator is bit-exact against the oracle,
 and the executor's bookkeeping (validation, slots, live counts, op log,
 error codes) matches the oracle on bookkeeping-only handles."""
 
+import ctypes
 import os
 import re
 import subprocess
@@ -207,3 +208,29 @@ def test_create_rejects_bad_descs():
         _bk_stage(4, 8, 0, block=pps.BLOCK_TOY_GELU, dtype=pps.DTYPE_BF16)
     with pytest.raises(pps.PpsError):
         pps.Stage(P=4, M=8, k=0, L=1, d=64, ffn=64, T=8)   # no weights without bookkeeping-only
+
+
+def test_simulate_pipeline_matches_oracle():
+    import random
+    from oracle import schedule as S
+    rng = random.Random(5)
+    cases = [(2, 4, 1, pps.GPIPE), (4, 6, 1, pps.ONE_F_ONE_B), (8, 16, 1, pps.ONE_F_ONE_B), (8, 16, 2, pps.ONE_F_ONE_B),
+             (4, 12, 3, pps.ONE_F_ONE_B), (4, 8, 1, pps.ZB1P), (4, 32, 1, pps.ZB2P), (5, 7, 1, pps.ZB1P)]
+    for P, M, v, kind in cases:
+        for _ in range(3):
+            tf, tb, tw = rng.uniform(0.1, 3), rng.uniform(0.1, 3), rng.uniform(0.1, 3)
+            mk, bubble = pps.simulate_pipeline(P, M, v, kind, tf, tb, tw)
+            ok, obub = S.simulate_timed(S.all_stage_lists(P, M, v, kind), {S.F: tf, S.B: tb, S.W: tw}, v)
+            assert mk == pytest.approx(ok, rel=1e-12), (P, M, v, kind)
+            assert bubble == pytest.approx(obub, rel=1e-9, abs=1e-12), (P, M, v, kind)
+
+
+def test_simulate_pipeline_errors():
+    mk = ctypes.c_double(0)
+    bu = ctypes.c_double(0)
+    L = pps.lib()
+    for args in [(4, 6, 1, pps.ONE_F_ONE_B, -1.0, 1.0, 0.0), (4, 6, 1, pps.ONE_F_ONE_B, float("nan"), 1.0, 0.0),
+                 (4, 6, 2, pps.ONE_F_ONE_B, 1.0, 1.0, 0.0), (0, 6, 1, pps.ONE_F_ONE_B, 1.0, 1.0, 0.0),
+                 (4, 6, 1, 9, 1.0, 1.0, 0.0), (4, 6, 1, pps.ONE_F_ONE_B, 1.0, float("inf"), 0.0)]:
+        assert L.pps_simulate_pipeline(*args, ctypes.byref(mk), ctypes.byref(bu)) == pps.EINVAL, args
+    assert L.pps_simulate_pipeline(4, 6, 1, pps.ONE_F_ONE_B, 1.0, 1.0, 0.0, None, ctypes.byref(bu)) == pps.EINVAL

@@ -294,3 +294,43 @@ def test_stage_ops_errors():
         S.stage_ops(4, 6, 0, 2)
     with pytest.raises(S.ScheduleError):
         S.stage_ops(4, 8, 0, 2, S.ZB1P)
+
+
+# ---- timed simulation (measured-cost prediction of the P-stage timeline) ----
+
+@pytest.mark.parametrize("kind", [S.GPIPE, S.ONE_F_ONE_B])
+@pytest.mark.parametrize("P,M", [(2, 4), (4, 6), (8, 16), (4, 32)])
+@pytest.mark.parametrize("tf,tb", [(1.0, 1.0), (1.0, 2.0), (0.7, 1.9), (2.5, 1.0)])
+def test_timed_closed_form(kind, P, M, tf, tb):
+    # [1F1B §4.3], [Sched §04]: the bubble is (P-1) of M+P-1 slots of t_f + t_b
+    # for both GPipe and 1F1B; [lpnh] quotes t_b ~ 2 t_f.  Transfers take no time.
+    mk, bubble = S.simulate_timed(S.all_stage_lists(P, M, 1, kind), {S.F: tf, S.B: tb, S.W: 0.0})
+    assert mk == pytest.approx((M + P - 1) * (tf + tb), rel=1e-12)
+    assert bubble == pytest.approx((P - 1) / (M + P - 1), rel=1e-9)
+
+
+@pytest.mark.parametrize("P,M,v,kind", [(4, 6, 1, S.ONE_F_ONE_B), (4, 8, 2, S.ONE_F_ONE_B), (8, 16, 2, S.ONE_F_ONE_B),
+                                        (4, 8, 1, S.ZB1P), (4, 32, 1, S.ZB2P), (3, 5, 1, S.GPIPE)])
+def test_timed_unit_costs_match_unit_simulator(P, M, v, kind):
+    lists = S.all_stage_lists(P, M, v, kind)
+    starts = S.simulate(lists, v)
+    mk, bubble = S.simulate_timed(lists, {S.F: 1, S.B: 1, S.W: 1}, v)
+    assert mk == S.total_time(starts)
+    assert bubble == pytest.approx(1.0 - S.busy_fraction(lists, starts), abs=1e-12)
+
+
+@pytest.mark.parametrize("P,M,v", [(4, 8, 2), (8, 16, 2), (4, 12, 3)])
+def test_timed_interleaved_bubble(P, M, v):
+    # [1F1B §6.1]: with v chunks per device the bubble is (P-1)/(vM+P-1)
+    _, bubble = S.simulate_timed(S.all_stage_lists(P, M, v, S.ONE_F_ONE_B), {S.F: 1, S.B: 1, S.W: 0}, v)
+    assert bubble == pytest.approx((P - 1) / (v * M + P - 1), rel=1e-12)
+
+
+@pytest.mark.parametrize("P,M", [(4, 8), (4, 32), (8, 16)])
+def test_timed_zero_bubble_not_longer(P, M):
+    # splitting B into dX then W can only fill gaps: never longer than 1F1B
+    # running the whole backward (dX + W) as one op ([GPipe->ZB Zero Bubble])
+    tf, tbx, tw = 1.0, 1.0, 1.0
+    mk_zb, _ = S.simulate_timed(S.all_stage_lists(P, M, 1, S.ZB1P), {S.F: tf, S.B: tbx, S.W: tw})
+    mk_1f1b, _ = S.simulate_timed(S.all_stage_lists(P, M, 1, S.ONE_F_ONE_B), {S.F: tf, S.B: tbx + tw, S.W: 0.0})
+    assert mk_zb <= mk_1f1b + 1e-12
