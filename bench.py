@@ -115,6 +115,9 @@ def main():
     ap.add_argument("--config", default="c3_80layer_p8_stage0")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--recompute", action="store_true",
+                    help="activation-recompute mode: a stash entry is the stage input alone and every "
+                         "backward re-runs the forward; value stays the algorithmic rate")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain fp32 copy kernel (pps_scale by 1.0) three times over this many MiB: "
                          "a reference of known size for the HBM byte counters")
@@ -158,6 +161,12 @@ def main():
     per_block_b = 7 if cfg.block == "swiglu" else 5
     launches_per_pass = cfg.M * cfg.v * cfg.L * (per_block_f + per_block_b) + 2 * cfg.M * cfg.v
     flags = 0 if args.no_profile else pps.FLAG_PROFILE
+    if args.recompute:
+        if cfg.block != "swiglu" or cfg.kind not in ("1f1b", "gpipe"):
+            print("--recompute needs SwiGLU blocks and a 1f1b or gpipe schedule", file=sys.stderr)
+            sys.exit(1)
+        flags |= pps.FLAG_RECOMPUTE
+        launches_per_pass += cfg.M * cfg.v * cfg.L * per_block_f
     st = pps.stage_from_config(cfg, weights=weights, stream=stream, flags=flags,
                                profile_capacity=launches_per_pass * (args.steps + 1))
     T, d = cfg.T, cfg.d
@@ -202,6 +211,9 @@ def main():
     ms_per_step = ms / args.steps
     flops_per_pass = cfg.flops_per_microbatch() * cfg.M
     tflops = flops_per_pass / (ms_per_step * 1e-3) / 1e12
+    # recompute: each backward re-runs the chunk's forward except the last down GEMM
+    extra = cfg.M * cfg.v * (6 * cfg.L - 2) * T * d * cfg.f if args.recompute else 0
+    executed_tflops = (flops_per_pass + extra) / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
     stats = st.stats()
 
@@ -233,7 +245,7 @@ def main():
     # The P-stage timeline this stage's measured per-op times imply (no
     # transfer time): every stage is assumed to cost what this one does.
     pipeline_model = None
-    if kernels and cfg.block == "swiglu" and cfg.v == 1:
+    if kernels and cfg.block == "swiglu" and cfg.v == 1 and not args.recompute:
         per_mb = lambda names: sum(kernels[n]["total_ms_per_step"] for n in names if n in kernels) / cfg.M
         t_f = per_mb(["rmsnorm_fwd", "gemm_gateup_swiglu", "gemm_down_residual"])
         t_bx = per_mb(["gemm_dh_swiglu_bwd", "gemm_dn", "rmsnorm_bwd_residual", "dgamma_reduce"])
@@ -272,12 +284,15 @@ def main():
                                f"{cfg.kind}{' v=' + str(cfg.v) if cfg.v > 1 else ''}, {cfg.L * cfg.v} SwiGLU blocks "
                                f"d={cfg.d} ffn={cfg.f}, {cfg.T} tokens/micro-batch",
                    "P": cfg.P, "M": cfg.M, "k": cfg.k, "v": cfg.v, "schedule": cfg.kind, "blocks": cfg.L * cfg.v,
-                   "d": cfg.d, "ffn": cfg.f, "tokens_per_microbatch": cfg.T, "ops_per_step": len(ops)},
+                   "d": cfg.d, "ffn": cfg.f, "tokens_per_microbatch": cfg.T, "ops_per_step": len(ops),
+                   "recompute": bool(args.recompute)},
         "peak_fraction": round(tflops / peak, 4),
         "peak_stash_bytes": stats["peak_live_bytes"],
         "peak_stash_entries": stats["peak_live_entries"],
         "stash_bound_entries": max(o[4] for o in ops),
         "flops_per_step": flops_per_pass,
+        "executed_flops_per_step": flops_per_pass + extra,
+        "executed_tflops": round(executed_tflops, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "pipeline_model": pipeline_model,

@@ -130,6 +130,17 @@ int pps_simulate_pipeline(int P, int M, int v, int kind, double t_f, double t_b,
                                         op log only: no device memory, no
                                         kernels, pointers are not touched     */
 #define PPS_FLAG_PROFILE          2u /* record HIP events around each kernel  */
+/* Activation recompute ([GPipe→ZB "GPipe 2018年"]: keep only the stage
+   boundary and redo each layer's forward when the backward reaches it;
+   [1F1B §4.5]: still advised under 1F1B).  A stash entry is then the stage
+   input x [T,d] alone, and pps_stage_backward first re-runs the chunk's
+   forward from it into one library-owned area (the per-block x, r, g, u of
+   a single micro-batch, shared by all backwards; the last block's output is
+   not recomputed: no backward reads it).  Kernels and launch shapes are the
+   forward's own, so every result is bit-identical to a run without the
+   flag.  SwiGLU blocks with kind GPIPE or 1F1B only (a deferred W would
+   need the recomputed tensors kept per micro-batch): PPS_EINVAL otherwise. */
+#define PPS_FLAG_RECOMPUTE        4u
 
 typedef struct pps_stage_desc {
     int32_t P, M, k, v, kind;   /* pipeline shape and schedule kind          */

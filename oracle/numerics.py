@@ -223,23 +223,34 @@ def full_batch_step(xs, dys, params, block="swiglu", eps=EPS):
     return np.split(Y, cut), np.split(DX, cut), acc
 
 
-def run_stage_ops(ops, xs, dys, params, block="swiglu", eps=EPS):
+def run_stage_ops(ops, xs, dys, params, block="swiglu", eps=EPS, recompute=False, trace=None):
     """Execute one stage's op list in order, as the executor does.
 
     ``ops`` is a list of (kind, mb, chunk) with kinds 0=F, 1=B, 2=W (only
     chunk 0 here).  A dict plays the activation stash: F stores, B pops
     ([1F1B §5.2] activations dict).  Gradients accumulate in op order.
+
+    ``recompute``: the stash keeps only the stage input, and B first runs the
+    forward again from it to get back what the blocks saved ([GPipe→ZB
+    "GPipe 2018年"]: only the boundary between devices is kept, each layer's
+    forward is redone when the backward reaches it).  Not defined with W ops.
+    ``trace``, if a list, receives after each op the number of stash entries
+    and the float64 elements they hold.
     Returns (ys, dxs, grads).
     """
     stash, pend = {}, {}
     ys, dxs = {}, {}
     acc = zero_grads(params)
     split = any(o[0] == 2 for o in ops)
+    assert not (split and recompute)
     for kind, i, _c in ops:
         if kind == 0:
-            ys[i], stash[i] = stage_forward(xs[i], params, block, eps)
+            ys[i], saved = stage_forward(xs[i], params, block, eps)
+            stash[i] = np.array(xs[i], dtype=np.float64, copy=True) if recompute else saved
         elif kind == 1:
             saved = stash.pop(i)
+            if recompute:
+                _, saved = stage_forward(saved, params, block, eps)
             dxs[i], ws_all, dgam = stage_backward_input(saved, dys[i], params, block)
             if split:
                 pend[i] = (ws_all, dgam)
@@ -248,6 +259,10 @@ def run_stage_ops(ops, xs, dys, params, block="swiglu", eps=EPS):
         else:
             ws_all, dgam = pend.pop(i)
             accumulate_weight_grads(acc, ws_all, dgam, block)
+        if trace is not None:
+            held = sum(e.size if recompute else sum(a.size for blk in e for a in blk.values())
+                       for e in stash.values())
+            trace.append((len(stash), held))
     assert not stash and not pend
     M = len(xs)
     return [ys[i] for i in range(M)], [dxs[i] for i in range(M)], acc
@@ -293,6 +308,12 @@ def rel_l2(a, ref):
     if den == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return float(num / den)
+
+
+def executed_flops_per_block_microbatch(T, d, f, recompute=False):
+    """GEMM FLOPs actually run per block per micro-batch: the algorithmic
+    18Tdf, plus the forward's 6Tdf again when B recomputes it."""
+    return (24 if recompute else 18) * T * d * f
 
 
 def flops_per_block_microbatch(T, d, f):

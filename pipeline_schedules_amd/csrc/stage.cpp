@@ -69,6 +69,10 @@ struct pps_stage {
     char* pool = nullptr;
     char* scratch = nullptr;
     size_t scratch_bytes = 0;
+    // recompute mode: slots hold the stage input only; the per-block tensors
+    // of the micro-batch being back-propagated live at scratch + s_rc
+    bool ac = false;
+    size_t s_rc = 0;
     size_t s_n = 0, s_h = 0, s_dgu = 0, s_dn = 0, s_dxa = 0, s_dxb = 0, s_part = 0, s_dz = 0;
     // bf16 path: K-contiguous operands of the weight-gradient GEMMs ([feature, Tp])
     size_t s_nT = 0, s_hT = 0, s_dguT = 0, s_dyT = 0;
@@ -99,6 +103,15 @@ namespace {
 int64_t T_(const pps_stage* h) { return h->d.T; }
 
 char* slot_base(pps_stage* h, int s) { return h->pool + (size_t)s * h->lay.slot_bytes; }
+
+// Base of the per-block forward tensors (offsets h->lay.x/r/g/u) of the
+// micro-batch in `slot`: the slot itself, or the shared recompute area.
+char* acts(pps_stage* h, int slot) { return h->ac ? h->scratch + h->s_rc : slot_base(h, slot); }
+
+// Block b's input; in recompute mode block 0's (the stage input) stays in the slot.
+char* act_x(pps_stage* h, int slot, int b) {
+    return (h->ac && b == 0) ? slot_base(h, slot) : acts(h, slot) + h->lay.x[b];
+}
 
 template <typename F>
 hipError_t timed(pps_stage* h, int kernel, double flops, double bytes, F&& launch) {
@@ -171,6 +184,9 @@ int validate_desc(const pps_stage_desc* d) {
     if (d->block_type == PPS_BLOCK_TOY_GELU && d->dtype != PPS_DTYPE_FP32) return PPS_EINVAL;
     if (d->L < 1 || d->d < 8 || d->d % 8 != 0 || d->d > 16384 || d->T < 0) return PPS_EINVAL;
     if (d->block_type == PPS_BLOCK_SWIGLU && (d->ffn < 8 || d->ffn % 8 != 0)) return PPS_EINVAL;
+    if ((d->flags & PPS_FLAG_RECOMPUTE) &&
+        (d->block_type != PPS_BLOCK_SWIGLU || d->kind == PPS_ZB1P || d->kind == PPS_ZB2P))
+        return PPS_EINVAL;
     if (!(d->eps >= 0.0f)) return PPS_EINVAL;
     if ((d->flags & PPS_FLAG_PROFILE) && d->profile_capacity < 0) return PPS_EINVAL;
     if (!(d->flags & PPS_FLAG_BOOKKEEPING_ONLY)) {
@@ -243,25 +259,30 @@ int refresh_weight_copies(pps_stage* h) {
     return PPS_OK;
 }
 
-int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_out) {
+// Forward of the chunk's blocks for the micro-batch in `slot`.  With
+// `recompute` (recompute mode, inside the backward) the input is the one the
+// slot already holds and y_out is unused: the last block's down GEMM, whose
+// output no backward reads, is skipped.
+int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_out, bool recompute = false) {
     const pps_stage_desc& D = h->d;
     const int64_t T = D.T, d = D.d, f = D.ffn;
     const int dt = D.dtype, es = h->es;
-    char* sb = slot_base(h, slot);
+    char* ab = acts(h, slot);
     char* sn = h->scratch + h->s_n;
     char* sh = h->scratch + h->s_h;
     const int blk0 = chunk * D.L;
     for (int b = 0; b < D.L; ++b) {
         const void* const* wb = h->w.data() + (size_t)(blk0 + b) * 4;
         const float* gamma = static_cast<const float*>(wb[3]);
-        char* xb = sb + h->lay.x[b];
-        float* rb = reinterpret_cast<float*>(sb + h->lay.r[b]);
-        char* gb = sb + h->lay.g[b];
-        char* ub = sb + h->lay.u[b];
-        const void* xin = b == 0 ? x_in : xb;
+        char* xb = act_x(h, slot, b);
+        float* rb = reinterpret_cast<float*>(ab + h->lay.r[b]);
+        char* gb = ab + h->lay.g[b];
+        char* ub = ab + h->lay.u[b];
+        const bool copy_in = b == 0 && !recompute;
+        const void* xin = copy_in ? x_in : xb;
         // r and n = x r gamma ([T,d]); block 0 also copies x into the stash.
-        PPS_TRY(timed(h, PPS_K_RMSNORM_FWD, 0.0, (double)T * d * es * (b == 0 ? 3 : 2) + T * 4.0 + d * 4.0, [&] {
-            return pps::rmsnorm_fwd(dt, xin, gamma, D.eps, T, d, rb, sn, b == 0 ? xb : nullptr, h->stream);
+        PPS_TRY(timed(h, PPS_K_RMSNORM_FWD, 0.0, (double)T * d * es * (copy_in ? 3 : 2) + T * 4.0 + d * 4.0, [&] {
+            return pps::rmsnorm_fwd(dt, xin, gamma, D.eps, T, d, rb, sn, copy_in ? xb : nullptr, h->stream);
         }));
         // g, u = n [Wg | Wu] with h = silu(g) u in the epilogue.
         GemmArgs a;
@@ -276,6 +297,7 @@ int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_
         a.epi = pps::EPI_SWIGLU;
         a.e.out0 = gb; a.e.out1 = ub; a.e.out2 = sh; a.e.ld0 = f;
         PPS_TRY(timed(h, PPS_K_GATEUP, gemm_flops(T, 2.0 * f, d), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
+        if (recompute && b == D.L - 1) break;
         // y = x + h Wd, written as the next block's x (or the stage output).
         GemmArgs c;
         c.M = T; c.N = d; c.nseg = 1;
@@ -287,7 +309,7 @@ int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_
             c.seg[0].B = wb[2]; c.seg[0].ldb = d; c.b_kcontig = false;
         }
         c.epi = pps::EPI_RESID;
-        c.e.out0 = b == D.L - 1 ? y_out : static_cast<void*>(sb + h->lay.x[b + 1]);
+        c.e.out0 = b == D.L - 1 ? y_out : static_cast<void*>(act_x(h, slot, b + 1));
         c.e.ld0 = d; c.e.in0 = xb; c.e.ldi0 = d;
         PPS_TRY(timed(h, PPS_K_DOWN, gemm_flops(T, d, f), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
     }
@@ -315,15 +337,15 @@ int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, cons
     const pps_stage_desc& D = h->d;
     const int64_t T = D.T, d = D.d, f = D.ffn, Tp = h->Tp;
     const int dt = D.dtype, es = h->es;
-    char* sb = slot_base(h, slot);
     const void* const* wb = h->w.data() + (size_t)(chunk * D.L + b) * 4;
     const float* gamma = static_cast<const float*>(wb[3]);
     const size_t gi = (size_t)(chunk * D.L + b) * 4;
     float* dWg = h->grads + h->goff[gi + 0];
     float* dWu = h->grads + h->goff[gi + 1];
     float* dWd = h->grads + h->goff[gi + 2];
-    const char* xb = sb + h->lay.x[b];
-    const float* rb = reinterpret_cast<const float*>(sb + h->lay.r[b]);
+    char* ab = acts(h, slot);
+    const char* xb = act_x(h, slot, b);
+    const float* rb = reinterpret_cast<const float*>(ab + h->lay.r[b]);
     GemmArgs a, c;
     if (h->tn) {
         char* nT = h->scratch + h->s_nT;
@@ -331,7 +353,7 @@ int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, cons
         PPS_TRY(timed(h, PPS_K_PREP_W, 0.0, (double)T * (2.0 * d + 2.0 * f) * es + (double)Tp * (d + f) * es, [&] {
             hipError_t e = pps::transpose(dt, 1, xb, nullptr, rb, gamma, T, d, d, nT, Tp, 0, 0, h->stream);
             if (e == hipSuccess)
-                e = pps::transpose(dt, 2, sb + h->lay.g[b], sb + h->lay.u[b], nullptr, nullptr, T, f, f, hT, Tp, 0, 0, h->stream);
+                e = pps::transpose(dt, 2, ab + h->lay.g[b], ab + h->lay.u[b], nullptr, nullptr, T, f, f, hT, Tp, 0, 0, h->stream);
             return e;
         }));
         a.seg[0].A = hT; a.seg[0].lda = Tp; a.seg[0].B = dy; a.seg[0].ldb = Tp;
@@ -342,7 +364,7 @@ int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, cons
         char* sn = h->scratch + h->s_n;
         char* sh = h->scratch + h->s_h;
         PPS_TRY(timed(h, PPS_K_PREP_W, 0.0, (double)T * (2.0 * d + 3.0 * f) * es + T * 4.0 + d * 4.0, [&] {
-            return pps::prep_w(dt, xb, rb, gamma, sb + h->lay.g[b], sb + h->lay.u[b], T, d, f, sn, sh, h->stream);
+            return pps::prep_w(dt, xb, rb, gamma, ab + h->lay.g[b], ab + h->lay.u[b], T, d, f, sn, sh, h->stream);
         }));
         a.seg[0].A = sh; a.seg[0].lda = f; a.seg[0].B = dy; a.seg[0].ldb = d;
         a.a_kcontig = false; a.b_kcontig = false;
@@ -368,6 +390,11 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
     char* dxbuf[2] = {h->scratch + h->s_dxa, h->scratch + h->s_dxb};
     float* dn = reinterpret_cast<float*>(h->scratch + h->s_dn);
     float* part = reinterpret_cast<float*>(h->scratch + h->s_part);
+    if (h->ac) {
+        int rc = swiglu_forward(h, slot, chunk, nullptr, nullptr, true);
+        if (rc != PPS_OK) return rc;
+    }
+    char* ab = acts(h, slot);
     if (h->split && !h->tn) {
         // Keep this micro-batch's output gradient for the deferred W.
         char* dst = sb + h->lay.dy[D.L - 1];
@@ -397,7 +424,7 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
         a.seg[0].B = wb[2]; a.seg[0].ldb = d;
         a.a_kcontig = true; a.b_kcontig = true;
         a.epi = pps::EPI_SWIGLU_BWD;
-        a.e.in0 = sb + h->lay.g[b]; a.e.in1 = sb + h->lay.u[b]; a.e.ldi0 = f;
+        a.e.in0 = ab + h->lay.g[b]; a.e.in1 = ab + h->lay.u[b]; a.e.ldi0 = f;
         a.e.out0 = dgu; a.e.ld0 = 2 * f; a.e.nsplit = f;
         PPS_TRY(timed(h, PPS_K_DH, gemm_flops(T, f, d), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
         // dn = dg Wg^T + du Wu^T (one accumulator, K = 2 ffn).
@@ -425,7 +452,7 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
         int nrows = 0;
         PPS_TRY(timed(h, PPS_K_RMSNORM_BWD, 0.0,
                       (double)T * d * 4 + 3.0 * T * d * es + T * 4.0 + d * 4.0 + (double)pps::rmsnorm_bwd_partial_rows(T) * d * 4, [&] {
-                          return pps::rmsnorm_bwd(dt, dn, sb + h->lay.x[b], reinterpret_cast<const float*>(sb + h->lay.r[b]),
+                          return pps::rmsnorm_bwd(dt, dn, act_x(h, slot, b), reinterpret_cast<const float*>(ab + h->lay.r[b]),
                                                   gamma, dy, T, d, dx, part, &nrows, h->stream);
                       }));
         const int prow = pps::rmsnorm_bwd_partial_rows(T);
@@ -548,6 +575,7 @@ extern "C" int pps_stage_create(const pps_stage_desc* desc, pps_stage** out) {
     h->nw = h->swiglu ? 4 : 2;
     h->es = desc->dtype == PPS_DTYPE_BF16 ? 2 : 4;
     h->split = desc->kind == PPS_ZB1P || desc->kind == PPS_ZB2P;
+    h->ac = (desc->flags & PPS_FLAG_RECOMPUTE) != 0;
     h->stream = static_cast<hipStream_t>(desc->stream);
     h->d.weights = nullptr;
     if (!h->bookkeeping) h->w.assign(desc->weights, desc->weights + (size_t)desc->v * desc->L * h->nw);
@@ -572,6 +600,12 @@ extern "C" int pps_stage_create(const pps_stage_desc* desc, pps_stage** out) {
     const size_t T = (size_t)desc->T, dm = (size_t)desc->d, f = (size_t)desc->ffn, Tp = (size_t)h->Tp;
     size_t off = 0;
     auto take = [&](size_t& o, size_t bytes) { o = off; off += align256(bytes); };
+    if (h->ac) {
+        // the block tensors move to the recompute area; a slot keeps x alone
+        take(h->s_rc, h->lay.fwd_bytes);
+        h->lay.fwd_bytes = align256(T * dm * h->es);
+        h->lay.slot_bytes = std::max<size_t>(h->lay.fwd_bytes, 256);
+    }
     if (h->swiglu) {
         take(h->s_n, T * dm * h->es);
         take(h->s_h, T * f * h->es);

@@ -22,7 +22,7 @@ OP_F, OP_B, OP_W = 0, 1, 2
 GPIPE, ONE_F_ONE_B, ZB1P, ZB2P = 0, 1, 2, 3
 BLOCK_SWIGLU, BLOCK_TOY_GELU = 0, 1
 DTYPE_BF16, DTYPE_FP32 = 0, 1
-FLAG_BOOKKEEPING_ONLY, FLAG_PROFILE = 1, 2
+FLAG_BOOKKEEPING_ONLY, FLAG_PROFILE, FLAG_RECOMPUTE = 1, 2, 4
 
 KIND_BY_NAME = {"gpipe": GPIPE, "1f1b": ONE_F_ONE_B, "zb1p": ZB1P, "zb2p": ZB2P}
 DTYPE_BY_NAME = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}

@@ -94,9 +94,9 @@ def test_make_schedule_errors():
 
 
 def _bk_stage(P, M, k, v=1, kind=pps.ONE_F_ONE_B, L=2, d=64, ffn=128, T=16, block=pps.BLOCK_SWIGLU,
-              dtype=pps.DTYPE_BF16):
+              dtype=pps.DTYPE_BF16, flags=0):
     return pps.Stage(P=P, M=M, k=k, v=v, kind=kind, block=block, dtype=dtype, L=L, d=d, ffn=ffn, T=T,
-                     flags=pps.FLAG_BOOKKEEPING_ONLY)
+                     flags=pps.FLAG_BOOKKEEPING_ONLY | flags)
 
 
 def _drive(stage, ops):
@@ -159,6 +159,40 @@ def test_bookkeeping_stash_bytes():
             live_b.discard(mb)
         peak = max(peak, len(live_f) * fwd + len(live_b) * extra)
     assert s["peak_live_bytes"] == peak
+
+
+@pytest.mark.parametrize("dtype,es", [(pps.DTYPE_BF16, 2), (pps.DTYPE_FP32, 4)])
+def test_bookkeeping_recompute_stash_bytes(dtype, es):
+    """Recompute mode: an entry is the stage input [T, d] alone; the per-block
+    tensors of one micro-batch move to library scratch."""
+    _lib_or_skip()
+    T, d, f, L = 24, 64, 128, 3
+    a = lambda b: (b + 255) // 256 * 256
+    full = L * (a(T * d * es) + a(T * 4) + 2 * a(T * f * es))
+    plain = _bk_stage(4, 8, 1, T=T, d=d, ffn=f, L=L, dtype=dtype)
+    ac = _bk_stage(4, 8, 1, T=T, d=d, ffn=f, L=L, dtype=dtype, flags=pps.FLAG_RECOMPUTE)
+    ops = S.stage_ops(4, 8, 1)
+    for st in (plain, ac):
+        _drive(st, ops)
+        assert st.oplog() == [tuple(o) for o in ops]
+    sp, sa = plain.stats(), ac.stats()
+    assert sp["slot_bytes"] == full
+    assert sa["slot_bytes"] == a(T * d * es) and sa["pool_bytes"] == 3 * a(T * d * es)
+    assert sa["peak_live_bytes"] == 3 * a(T * d * es)          # P - k entries
+    assert sa["scratch_bytes"] == sp["scratch_bytes"] + full
+    for st in (plain, ac):
+        st.close()
+
+
+def test_recompute_rejected_where_undefined():
+    _lib_or_skip()
+    for kind in (pps.ZB1P, pps.ZB2P):
+        with pytest.raises(pps.PpsError):
+            _bk_stage(4, 8, 0, kind=kind, flags=pps.FLAG_RECOMPUTE)
+    with pytest.raises(pps.PpsError):
+        _bk_stage(4, 8, 0, block=pps.BLOCK_TOY_GELU, dtype=pps.DTYPE_FP32, flags=pps.FLAG_RECOMPUTE)
+    for kind, v in ((pps.GPIPE, 1), (pps.ONE_F_ONE_B, 2)):
+        _bk_stage(4, 8, 0, v=v, kind=kind, flags=pps.FLAG_RECOMPUTE).close()
 
 
 def test_bookkeeping_error_codes():

@@ -42,7 +42,7 @@ def _cfg(name, d, f, kind, P):
     return StageConfig(name, P=P, M=2, k=0, v=1, kind=kind, block="swiglu", dtype="bf16", L=2, d=d, f=f, T=8192)
 
 
-def _run(env, cfg):
+def _run(env, cfg, flags=0):
     torch, pps = env
     from pipeline_schedules_amd.inputs import make_device_inputs
 
@@ -66,7 +66,7 @@ def _run(env, cfg):
     for p in inp["params"]:
         weights += [p["Wg"], p["Wu"], p["Wd"], p["gamma"]]
     stream = torch.cuda.current_stream()
-    st = pps.stage_from_config(cfg, weights=weights, stream=stream)
+    st = pps.stage_from_config(cfg, weights=weights, stream=stream, flags=flags)
     ops = pps.make_schedule(cfg.P, cfg.M, cfg.k, cfg.v, pps.KIND_BY_NAME[cfg.kind])
     ys = [torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=dev) for _ in range(cfg.M)]
     dxs = [torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=dev) for _ in range(cfg.M)]
@@ -87,9 +87,9 @@ def _host(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def _check(env, cfg):
+def _check(env, cfg, flags=0):
     torch, pps = env
-    inp, rows, st, ys, dxs = _run(env, cfg)
+    inp, rows, st, ys, dxs = _run(env, cfg, flags)
 
     # the oracle on the sampled rows only (token-local blocks; pipelined order = full batch)
     xs_h = [_host(inp["xs"][i][torch.from_numpy(rows[i]).cuda()]) for i in range(cfg.M)]
@@ -131,3 +131,8 @@ def test_80layer_slice_shapes_1f1b(env):
 def test_zero_bubble_shapes_split(env):
     """T=8192, d=4096, ffn=14336, ZB1P: dX in B, dW deferred to W."""
     _check(env, _cfg("c5-shapes", 4096, 14336, "zb1p", 4))
+
+
+def test_80layer_slice_shapes_recompute(env):
+    """The same stage in recompute mode (each B re-runs the forward from x)."""
+    _check(env, _cfg("c3-shapes-recompute", 8192, 28672, "1f1b", 8), flags=env[1].FLAG_RECOMPUTE)

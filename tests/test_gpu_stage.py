@@ -36,10 +36,10 @@ def _oracle_kind(name):
     return {"1f1b": S.ONE_F_ONE_B, "gpipe": S.GPIPE, "zb1p": S.ZB1P, "zb2p": S.ZB2P}[name]
 
 
-def _run_single(env, cfg, inp, kind):
+def _run_single(env, cfg, inp, kind, flags=0):
     torch, pps, G = env
     w = G.upload_params(inp.params[0], cfg.block, cfg.dtype)
-    st = pps.stage_from_config(cfg, weights=w, kind=kind, stream=torch.cuda.current_stream())
+    st = pps.stage_from_config(cfg, weights=w, kind=kind, stream=torch.cuda.current_stream(), flags=flags)
     ops = pps.make_schedule(cfg.P, cfg.M, cfg.k, cfg.v, pps.KIND_BY_NAME[kind])
     assert ops == [tuple(o) for o in S.stage_ops(cfg.P, cfg.M, cfg.k, cfg.v, _oracle_kind(kind))]
     xs = [[G.to_dev(x, cfg.dtype) for x in inp.xs]]
@@ -96,6 +96,30 @@ def test_split_is_bit_identical_to_unsplit(env):
     assert b[3]["peak_live_bytes"] > a[3]["peak_live_bytes"]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("kind", ["1f1b", "gpipe"])
+def test_recompute_mode(env, dtype, kind):
+    # Recompute mode: parity with the oracle, bit-identical to the run that
+    # keeps the forward's tensors, and a stash entry of x [T, d] alone.
+    torch, pps, G = env
+    from pipeline_schedules_amd.inputs import make_inputs
+    cfg = _swiglu_cfg(dtype, M=5, P=3, L=3, kind=kind)
+    inp = make_inputs(cfg, gamma="random")
+    a = _run_single(env, cfg, inp, kind)
+    r = _run_single(env, cfg, inp, kind, flags=pps.FLAG_RECOMPUTE)
+    _check(cfg, r, inp, TOL[dtype])
+    for i in range(cfg.M):
+        assert np.array_equal(a[0][i], r[0][i]) and np.array_equal(a[1][i], r[1][i]), i
+    for blk in range(cfg.L):
+        for key in a[2][blk]:
+            assert np.array_equal(a[2][blk][key], r[2][blk][key]), (blk, key)
+    es = 2 if dtype == "bf16" else 4
+    entry = (cfg.T * cfg.d * es + 255) // 256 * 256
+    peak = cfg.P - cfg.k if kind == "1f1b" else cfg.M
+    assert r[3]["slot_bytes"] == entry and r[3]["peak_live_bytes"] == peak * entry
+    assert a[3]["peak_live_bytes"] > cfg.L * r[3]["peak_live_bytes"]
+
+
 def test_orders_agree_with_full_batch(env):
     # 1F1B order, GPipe order and the full-batch oracle give the same result
     # ([1F1B §4.5]: synchronous 1F1B equals one large-batch step).
@@ -124,7 +148,8 @@ def test_toy_stage_parity(env, kind):
     _check(C1_TOY, got, inp, TOL["fp32"])
 
 
-def test_interleaved_stage_parity(env):
+@pytest.mark.parametrize("recompute", [False, True])
+def test_interleaved_stage_parity(env, recompute):
     torch, pps, G = env
     from pipeline_schedules_amd.inputs import make_inputs
     cfg = _swiglu_cfg("bf16", T=264, d=264, f=392, L=1, M=4, P=2, k=0, v=2)
@@ -134,7 +159,8 @@ def test_interleaved_stage_parity(env):
     xs1 = [np.asarray(x) for x in make_inputs(cfg, rng_seed=1).xs]
     gs1 = [np.asarray(g) for g in make_inputs(cfg, rng_seed=2).Gs]
     w = G.upload_params(inp.params[0], "swiglu", "bf16")
-    st = pps.stage_from_config(cfg, weights=w, stream=torch.cuda.current_stream())
+    st = pps.stage_from_config(cfg, weights=w, stream=torch.cuda.current_stream(),
+                               flags=pps.FLAG_RECOMPUTE if recompute else 0)
     ops = pps.make_schedule(cfg.P, cfg.M, cfg.k, 2, pps.ONE_F_ONE_B)
     assert ops == [tuple(o) for o in S.stage_ops(cfg.P, cfg.M, cfg.k, 2, S.ONE_F_ONE_B)]
     xs = [[G.to_dev(x, "bf16") for x in inp.xs], [G.to_dev(x, "bf16") for x in xs1]]

@@ -247,6 +247,44 @@ def test_pipelined_orders_equal_full_batch(block):
                 assert N.rel_l2(g[b][key], g_f[b][key]) < 1e-13, (name, b, key)
 
 
+@pytest.mark.parametrize("block", ["swiglu", "toy"])
+def test_recompute_mode_equals_stash_mode(block):
+    # Recomputing the forward inside B from the stashed stage input gives the
+    # very arrays the forward saved, so every result is bit-identical; the
+    # stash then holds T*d elements per entry whatever the depth L, against
+    # L blocks' worth when the forward's tensors are kept.
+    rng = np.random.default_rng(12)
+    P, M, k, T, d, f = 4, 6, 1, 5, 8, 12
+    held_per_entry = {}
+    for L in (1, 3):
+        params = ([_rand_swiglu(rng, d, f) for _ in range(L)] if block == "swiglu"
+                  else _toy_cfg_params(rng, L, d))
+        xs = [rng.normal(0, 1, (T, d)) for _ in range(M)]
+        dys = [rng.normal(0, 1, (T, d)) for _ in range(M)]
+        for ops, peak in ((S.one_f_one_b(P, M, k), P - k), (S.gpipe(P, M, k), M)):
+            tr_s, tr_r = [], []
+            ys, dxs, g = N.run_stage_ops(ops, xs, dys, params, block, trace=tr_s)
+            ys_r, dxs_r, g_r = N.run_stage_ops(ops, xs, dys, params, block, recompute=True, trace=tr_r)
+            for i in range(M):
+                assert np.array_equal(ys[i], ys_r[i]) and np.array_equal(dxs[i], dxs_r[i])
+            for b in range(L):
+                for key in g[b]:
+                    assert np.array_equal(g[b][key], g_r[b][key]), (L, b, key)
+            assert [n for n, _ in tr_s] == [n for n, _ in tr_r]
+            assert max(n for n, _ in tr_r) == peak
+            for n, held in tr_r:
+                assert held == n * T * d
+            per = {held // n for n, held in tr_s if n}
+            assert len(per) == 1
+            held_per_entry[L] = per.pop()
+    if block == "swiglu":   # x, n [T,d]; r [T]; g, u, h [T,f] per block
+        per_block = 2 * T * d + T + 3 * T * f
+    else:                   # x, z [T,d] per block
+        per_block = 2 * T * d
+    assert held_per_entry == {1: per_block, 3: 3 * per_block}
+    assert N.executed_flops_per_block_microbatch(T, d, f, True) / N.flops_per_block_microbatch(T, d, f) == 4 / 3
+
+
 def test_token_independence():
     # Rows are independent: the forward of a batch is the row-concatenation
     # of the forwards of its parts.
