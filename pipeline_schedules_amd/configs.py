@@ -20,7 +20,7 @@ class StageConfig:
     M: int
     k: int
     v: int
-    kind: str          # "1f1b" (interleaved when v > 1), "gpipe", "zb1p"
+    kind: str          # "1f1b" (interleaved when v > 1), "gpipe", "zb1p", "zb2p"
     block: str         # "swiglu" or "toy"
     dtype: str         # "bf16" or "fp32"
     L: int             # blocks per chunk
@@ -73,4 +73,7 @@ C4_INTERLEAVED = C3_SLICE.with_(name="c4_80layer_p8_v2", v=2, L=5)
 C5_ZB = StageConfig("c5_zb1p_p4m32", P=4, M=32, k=0, v=1, kind="zb1p",
                     block="swiglu", dtype="bf16", L=8, d=4096, f=14336, T=8192)
 
-PRESETS = {c.name: c for c in (C1_TOY, C2_SMALL, C3_SLICE, C4_INTERLEAVED, C5_ZB)}
+# The same stage under ZB2P (W budget 2(P-k), larger stash).
+C6_ZB2P = C5_ZB.with_(name="c6_zb2p_p4m32", kind="zb2p")
+
+PRESETS = {c.name: c for c in (C1_TOY, C2_SMALL, C3_SLICE, C4_INTERLEAVED, C5_ZB, C6_ZB2P)}

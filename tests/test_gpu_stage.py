@@ -71,7 +71,7 @@ def _check(cfg, got, inp, tol):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("kind", ["1f1b", "gpipe", "zb1p"])
+@pytest.mark.parametrize("kind", ["1f1b", "gpipe", "zb1p", "zb2p"])
 def test_swiglu_stage_parity(env, dtype, kind):
     from pipeline_schedules_amd.inputs import make_inputs
     cfg = _swiglu_cfg(dtype, kind=kind)
@@ -139,7 +139,7 @@ def test_orders_agree_with_full_batch(env):
     assert a[3]["peak_live_entries"] == 3 and g[3]["peak_live_entries"] == 4
 
 
-@pytest.mark.parametrize("kind", ["1f1b", "gpipe", "zb1p"])
+@pytest.mark.parametrize("kind", ["1f1b", "gpipe", "zb1p", "zb2p"])
 def test_toy_stage_parity(env, kind):
     from pipeline_schedules_amd.configs import C1_TOY
     from pipeline_schedules_amd.inputs import make_inputs
