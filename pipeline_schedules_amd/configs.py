@@ -76,4 +76,7 @@ C5_ZB = StageConfig("c5_zb1p_p4m32", P=4, M=32, k=0, v=1, kind="zb1p",
 # The same stage under ZB2P (W budget 2(P-k), larger stash).
 C6_ZB2P = C5_ZB.with_(name="c6_zb2p_p4m32", kind="zb2p")
 
-PRESETS = {c.name: c for c in (C1_TOY, C2_SMALL, C3_SLICE, C4_INTERLEAVED, C5_ZB, C6_ZB2P)}
+# The same stage unsplit (plain 1F1B): the reference point for the cost of the split.
+C5_UNSPLIT = C5_ZB.with_(name="c5u_1f1b_p4m32", kind="1f1b")
+
+PRESETS = {c.name: c for c in (C1_TOY, C2_SMALL, C3_SLICE, C4_INTERLEAVED, C5_ZB, C6_ZB2P, C5_UNSPLIT)}
