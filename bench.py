@@ -124,7 +124,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one pipeline stage on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU transport between stages is not part of this build)", file=sys.stderr)
+              "(the multi-GPU transport between stages is not implemented)", file=sys.stderr)
         sys.exit(1)
 
     import torch

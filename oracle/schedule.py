@@ -8,7 +8,7 @@ An *op* is a tuple ``(kind, mb, chunk)`` with kind F=0 (forward), B=1
 (backward; input gradient, and also the weight gradient unless the
 Zero-Bubble split is on) or W=2 (deferred weight gradient).
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
   * warmup length: [1F1B §2.3/§3.2] warms up P-k forwards then alternates
     B,F; [Megatron-PP 三阶段] warms up P-k-1 forwards then alternates F,B.
     Both give the same op order (``megatron_1f1b`` proves it in tests).
