@@ -10,12 +10,14 @@
 // grid, 128 x 64 per wavefront = 4 x 2 tiles of v_mfma_f32_32x32x16_bf16
 // (128 fp32 accumulators per lane, two wavefronts per SIMD).
 //
-// Data path: every operand tile is requested two K steps before it is
-// multiplied, and the requests are spread over the MFMAs of the step (a
-// stalled load issue then never idles the matrix core).  A goes straight to
-// LDS (direct-to-LDS buffer loads) into three 32 KB slots; B goes through two
-// register sets into two 32 KB slots (160 KB of LDS in all).  One barrier per
-// K step; MFMA operands are read with ds_read_b128.  In LDS, 16-byte chunk c
+// Data path: both operands go straight from memory to LDS (direct-to-LDS
+// buffer loads, no register staging).  A tiles are requested two K steps
+// before they are multiplied, into three 32 KB slots; B tiles one step ahead,
+// into two 32 KB slots (160 KB of LDS in all); the requests are spread over
+// the MFMAs of the step.  One barrier per K step; MFMA operands are read with
+// ds_read_b128.  The stage's GEMMs run at the chip's power limit, so what the
+// loop saves is energy: no register round trip and no LDS store instructions
+// for the operands.  In LDS, 16-byte chunk c
 // of row r sits at position c ^ ((r >> 1) & 7), which keeps the 16 lanes of
 // every ds_read_b128 phase on distinct banks (64 banks, two 128-byte rows
 // per bank period).  Buffer loads return zero outside the operand's extent,
@@ -239,22 +241,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (LDS_AS void*)(st + (wave_s * 4 + q) * 1024), 16, ao,
                                                  (uint32_t)kt * (BK * 2), 0, 0);
     };
-    auto issueB = [&](int kt, int q, uint4 (&rb)[4]) {
+    auto issueB = [&](int kt, int q) {
+        char* st = smem + BBASE + (kt & 1) * OPB;
         const uint32_t bo = lcq[q] < chunks_left(kt) ? boff[q] : OOB;
-        auto v = __builtin_amdgcn_raw_buffer_load_b128(br, bo, (uint32_t)kt * (BK * 2), 0);
-        rb[q] = *reinterpret_cast<uint4*>(&v);
-    };
-    // B pieces reach LDS through inline stores, so the compiler does not make
-    // them wait for the in-flight direct A loads (which target other slots).
-    const uint32_t bl0 = (uint32_t)(uintptr_t)(smem + BBASE + (wave * 4) * 1024 + lane * 16);
-    auto bstore = [&](int kt, const uint4 (&rb)[4]) {
-        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-        const uint32_t a = bl0 + (uint32_t)((kt & 1) * OPB);
-        asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:1024\n\t"
-                     "ds_write_b128 %0, %3 offset:2048\n\tds_write_b128 %0, %4 offset:3072"
-                     :: "v"(a), "v"(__builtin_bit_cast(u32x4, rb[0])), "v"(__builtin_bit_cast(u32x4, rb[1])),
-                        "v"(__builtin_bit_cast(u32x4, rb[2])), "v"(__builtin_bit_cast(u32x4, rb[3]))
-                     : "memory");
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (LDS_AS void*)(st + (wave_s * 4 + q) * 1024), 16, bo,
+                                                 (uint32_t)kt * (BK * 2), 0, 0);
     };
 
     // MFMA operand fragment: row r, logical chunk ch at r*128 + (ch ^ ((r>>1)&7))*16.
@@ -279,16 +270,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // One K step: multiply tile kt while tile kt+2 is requested (its A pieces
-    // into LDS slot (kt+2)%3, its B pieces into rfill, which held tile kt);
-    // then store tile kt+1's B (in rnext since the previous step) and barrier.
-    auto step = [&](int kt, uint4 (&rnext)[4], uint4 (&rfill)[4]) {
+    // One K step: multiply tile kt while tile kt+1's B (sub-steps 0, 1: its
+    // slot was last read before the previous barrier) and tile kt+2's A
+    // (sub-steps 2, 3) are requested; the barrier waits for all but the last
+    // four requests (tile kt+2's A).
+    auto step = [&](int kt) {
         bf16x8 fa[2][4], fb[2][2];
         frags(kt, 0, fa[0], fb[0]);
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            issueA(kt + 2, kk);
-            issueB(kt + 2, kk, rfill);
+            if (kk < 2) { issueB(kt + 1, 2 * kk); issueB(kt + 1, 2 * kk + 1); }
+            else { issueA(kt + 2, 2 * (kk - 2)); issueA(kt + 2, 2 * (kk - 2) + 1); }
             if (kk + 1 < BK / 16) frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
             // keep the next sub-step's fragment reads ahead of this sub-step's
             // MFMAs (left alone, the scheduler sinks them to their use)
@@ -299,11 +291,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
         }
-        bstore(kt + 1, rnext);   // the compiler waits for rnext's loads first
-        // vmcnt(8): everything but this step's 8 loads has landed, i.e. tile
-        // kt+1's A pieces; lgkmcnt(0): the B stores and this step's reads are
-        // done.  A bare barrier: a fence would also wait for tile kt+2.
-        wait_vm_lgkm0<8>();
+        // vmcnt(4): all but tile kt+2's four A requests have landed, i.e. tile
+        // kt+1; lgkmcnt(0): this step's fragment reads are done.  A bare
+        // barrier: a fence would also wait for tile kt+2.
+        wait_vm_lgkm0<4>();
         __builtin_amdgcn_s_barrier();
     };
 
@@ -328,27 +319,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         }
     };
 
-    uint4 rB[2][4];
     for (int s = 0; s < p.nseg; ++s) {
         set_seg(s);
         const int nk = (int)((K + BK - 1) / BK);
         if (nk == 0) continue;
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
+        for (int q = 0; q < 4; ++q) { issueA(0, q); issueB(0, q); }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) issueA(t2, q);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) issueB(t2, q, rB[t2]);
-        }
-        bstore(0, rB[0]);
-        wait_vm_lgkm0<8>();   // tile 0 complete (A in LDS, B stored)
+        for (int q = 0; q < 4; ++q) issueA(1, q);
+        wait_vm_lgkm0<4>();   // tile 0 in LDS
         __builtin_amdgcn_s_barrier();
-        const int nk2 = (nk + 1) & ~1;   // an odd count runs one all-zero tile
-        for (int kt = 0; kt < nk2; kt += 2) {
-            step(kt, rB[1], rB[0]);
-            step(kt + 1, rB[0], rB[1]);
-        }
-        // the last steps requested two all-zero tiles past K: let them land
+        for (int kt = 0; kt < nk; ++kt) step(kt);
+        // the last steps requested all-zero tiles past K: let them land
         // before another segment reuses the slots (and before the epilogue)
         wait_vm_lgkm0<0>();
         __builtin_amdgcn_s_barrier();
