@@ -36,10 +36,10 @@ PEAK_HBM_GBS = 8000.0
 # copy kernel measured in the same runs).  Valid only for the GEMM source they were taken on.
 TRAFFIC = {
     "config": "c3_80layer_p8_stage0",
-    "gemm_source_sha1": "46092042c6ad230948b95ae8eb695866deb55736",
+    "gemm_source_sha1": "20cfdcab728f7710c5e2c665b442bb2adbe27179",
     "bytes_per_launch": {
-        "gemm_gateup_swiglu": 14.110e9, "gemm_down_residual": 5.906e9, "gemm_dh_swiglu_bwd": 7.699e9,
-        "gemm_dn": 11.670e9, "gemm_wgrad_down": 7.535e9, "gemm_wgrad_gateup": 15.270e9,
+        "gemm_gateup_swiglu": 13.078e9, "gemm_down_residual": 5.908e9, "gemm_dh_swiglu_bwd": 7.539e9,
+        "gemm_dn": 11.585e9, "gemm_wgrad_down": 7.519e9, "gemm_wgrad_gateup": 15.205e9,
     },
 }
 
