@@ -172,6 +172,10 @@ typedef struct pps_stage pps_stage;
  * to the schedule's peak live count (P-k for 1F1B; M for GPipe) and
  * allocates, once, on the current device: the pool, scratch and the fp32
  * gradient buffers (library-owned, zeroed).  Nothing is allocated later.
+ * Limits: d a multiple of 8 up to 16384, ffn a multiple of 8; with bf16
+ * SwiGLU blocks every GEMM operand must stay under 2 GiB (T * 2ffn and
+ * 2*ceil(ffn/32)*32 * d elements of 2 bytes), since the MFMA kernel
+ * addresses operands with 32-bit offsets.
  * Returns PPS_EINVAL (bad desc), PPS_ENOMEM, PPS_EHIP.  *out is set only
  * on success.
  */

@@ -242,6 +242,13 @@ def test_create_rejects_bad_descs():
         _bk_stage(4, 8, 0, block=pps.BLOCK_TOY_GELU, dtype=pps.DTYPE_BF16)
     with pytest.raises(pps.PpsError):
         pps.Stage(P=4, M=8, k=0, L=1, d=64, ffn=64, T=8)   # no weights without bookkeeping-only
+    # bf16 GEMM operands are addressed with 32-bit byte offsets: dg|du [T, 2 ffn] must stay under 2 GiB
+    _bk_stage(8, 16, 0, d=8192, ffn=28672, T=8192)          # the 80-layer slice: 0.94 GB, accepted
+    with pytest.raises(pps.PpsError):
+        _bk_stage(8, 16, 0, d=8192, ffn=28672, T=32768)     # 3.76 GB
+    with pytest.raises(pps.PpsError):
+        _bk_stage(8, 16, 0, d=16384, ffn=65536, T=8)        # interleaved gate/up copy 4.3 GB
+    _bk_stage(8, 16, 0, d=8192, ffn=28672, T=32768, dtype=pps.DTYPE_FP32)   # the fp32 path has no such limit
 
 
 def test_simulate_pipeline_matches_oracle():
