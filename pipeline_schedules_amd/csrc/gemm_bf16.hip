@@ -27,6 +27,8 @@
 // ids are remapped so each XCD gets a contiguous run of logical tiles, and
 // logical tiles are ordered in groups of 8 tile-rows so the tiles running on
 // one XCD share A rows and B columns in that XCD's L2.
+#include <type_traits>
+
 #include "epilogue.h"
 
 namespace pps {
@@ -129,61 +131,67 @@ __device__ __forceinline__ float* acc_ptr(const EpiArgs& e, int64_t row, int64_t
                           : static_cast<float*>(e.out1) + row * e.ld1 + (col - e.nsplit);
 }
 
+// The epilogue's memory operands for four consecutive output columns of one
+// row: i0/i1 the inputs read, o0/o1/o2 the outputs written (which ones a role
+// uses is fixed by EPI; unused pointers are ignored).
+struct EpiPtr {
+    const char* i0;
+    const char* i1;
+    char* o0;
+    char* o1;
+    char* o2;
+};
+
 template <int EPI>
-__device__ __forceinline__ void epi_load(const EpiArgs& e, int64_t row, int64_t col, EpiIn<EPI>& in) {
+__device__ __forceinline__ void epi_load(const EpiPtr& a, EpiIn<EPI>& in) {
     if constexpr (EPI == EPI_RESID) {
-        in.x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(e.in0) + row * e.ldi0 + col);
+        in.x = *reinterpret_cast<const uint2*>(a.i0);
     } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-        in.g = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(e.in0) + row * e.ldi0 + col);
-        in.u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(e.in1) + row * e.ldi0 + col);
+        in.g = *reinterpret_cast<const uint2*>(a.i0);
+        in.u = *reinterpret_cast<const uint2*>(a.i1);
     } else if constexpr (EPI == EPI_ACC_F32) {
-        in.c = *reinterpret_cast<const float4*>(acc_ptr(e, row, col));
+        in.c = *reinterpret_cast<const float4*>(a.i0);
     }
 }
 
-// Four consecutive output columns col..col+3 of one row.
 template <int EPI>
-__device__ __forceinline__ void epi4(const EpiArgs& e, int64_t row, int64_t col, const float (&w)[4],
-                                     const EpiIn<EPI>& in) {
+__device__ __forceinline__ void epi4(const EpiPtr& a, const float (&w)[4], const EpiIn<EPI>& in) {
     if constexpr (EPI == EPI_STORE_F32) {
-        *reinterpret_cast<float4*>(static_cast<float*>(e.out0) + row * e.ld0 + col) = make_float4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<float4*>(a.o0) = make_float4(w[0], w[1], w[2], w[3]);
     } else if constexpr (EPI == EPI_STORE) {
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out0) + row * e.ld0 + col) = pack4(w);
+        *reinterpret_cast<uint2*>(a.o0) = pack4(w);
     } else if constexpr (EPI == EPI_RESID) {
         float x[4], y[4];
         unpack4(in.x, x);
 #pragma unroll
         for (int k = 0; k < 4; ++k) y[k] = x[k] + w[k];
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out0) + row * e.ld0 + col) = pack4(y);
+        *reinterpret_cast<uint2*>(a.o0) = pack4(y);
     } else if constexpr (EPI == EPI_SWIGLU_BWD) {
         float g[4], u[4], dg[4], du[4];
         unpack4(in.g, g);
         unpack4(in.u, u);
 #pragma unroll
         for (int k = 0; k < 4; ++k) swiglu_bwd_f(w[k], g[k], u[k], dg[k], du[k]);
-        uint16_t* o = static_cast<uint16_t*>(e.out0) + row * e.ld0;
-        *reinterpret_cast<uint2*>(o + col) = pack4(dg);
-        *reinterpret_cast<uint2*>(o + e.nsplit + col) = pack4(du);
+        *reinterpret_cast<uint2*>(a.o0) = pack4(dg);
+        *reinterpret_cast<uint2*>(a.o1) = pack4(du);
     } else if constexpr (EPI == EPI_ACC_F32) {
         const float4 c = in.c;
-        *reinterpret_cast<float4*>(acc_ptr(e, row, col)) = make_float4(c.x + w[0], c.y + w[1], c.z + w[2], c.w + w[3]);
+        *reinterpret_cast<float4*>(a.o0) = make_float4(c.x + w[0], c.y + w[1], c.z + w[2], c.w + w[3]);
     }
 }
 
 // Gate/up pair for hidden columns col..col+3: stores g, u (bf16) and
 // h = silu(g) u computed from the stored values.
-__device__ __forceinline__ void epi4_swiglu(const EpiArgs& e, int64_t row, int64_t col, const float (&g)[4],
-                                            const float (&u)[4]) {
+__device__ __forceinline__ void epi4_swiglu(const EpiPtr& a, const float (&g)[4], const float (&u)[4]) {
     const uint2 gp = pack4(g), up = pack4(u);
     float gs[4], us[4], hh[4];
     unpack4(gp, gs);
     unpack4(up, us);
 #pragma unroll
     for (int k = 0; k < 4; ++k) hh[k] = swiglu_f(gs[k], us[k]);
-    const int64_t o = row * e.ld0 + col;
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out0) + o) = gp;
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out1) + o) = up;
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(e.out2) + o) = pack4(hh);
+    *reinterpret_cast<uint2*>(a.o0) = gp;
+    *reinterpret_cast<uint2*>(a.o1) = up;
+    *reinterpret_cast<uint2*>(a.o2) = pack4(hh);
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt left at its maximum).
@@ -298,27 +306,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         __builtin_amdgcn_s_barrier();
     };
 
-    // Epilogue on quad-transposed accumulators: this lane owns row
-    // ... + q*8 + (l/32)*4 + l%4 and columns cq..cq+3 of each 32x32 tile.
-    const int jq = lane & 3;
-    const int cq = (lane & 31) & ~3;
-    const int64_t rbase = m0 + wm * 128 + (lane >> 5) * 4 + jq;
-    constexpr int PD = EPI == EPI_RESID ? 2 : 1;   // row groups loaded ahead (registers allow)
-    EpiIn<EPI> in[PD + 1][4][2];
-    auto prefetch = [&](int i, EpiIn<EPI> (&dst)[4][2]) {
-        if constexpr (EPI == EPI_RESID || EPI == EPI_SWIGLU_BWD || EPI == EPI_ACC_F32) {
-#pragma clang loop unroll(full)
-            for (int q = 0; q < 4; ++q) {
-                const int64_t row = rbase + i * 32 + q * 8;
-#pragma clang loop unroll(full)
-                for (int j = 0; j < 2; ++j) {
-                    const int64_t col = n0 + wn * 64 + j * 32 + cq;
-                    if (row < p.M && col < p.N) epi_load<EPI>(p.e, row, col, dst[q][j]);
-                }
-            }
-        }
-    };
-
     for (int s = 0; s < p.nseg; ++s) {
         set_seg(s);
         const int nk = (int)((K + BK - 1) / BK);
@@ -335,38 +322,128 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         wait_vm_lgkm0<0>();
         __builtin_amdgcn_s_barrier();
     }
-#pragma clang loop unroll(full)
-    for (int i = 0; i < PD; ++i) prefetch(i, in[i]);
+    // Epilogue on quad-transposed accumulators: this lane owns tile row
+    // lr + i*32 + q*8 and tile columns lc + j*32 .. +3 of each 32x32 tile.
+    const int jq = lane & 3;
+    const int cq = (lane & 31) & ~3;
+    const int lr = wm * 128 + (lane >> 5) * 4 + jq;
+    const int lc = (p.swiglu ? wn * 32 : wn * 64) + cq;
+    const EpiArgs& e = p.e;
+    constexpr int ESO = (EPI == EPI_STORE_F32 || EPI == EPI_ACC_F32) ? 4 : 2;   // output element bytes
+    constexpr bool HAS_IN = EPI == EPI_RESID || EPI == EPI_SWIGLU_BWD || EPI == EPI_ACC_F32;
+    constexpr int PD = EPI == EPI_RESID ? 2 : 1;   // row groups loaded ahead (registers allow)
+    EpiIn<EPI> in[PD + 1][4][2];
 
-
-
-#pragma clang loop unroll(full)
-    for (int i = 0; i < 4; ++i) {
-        if (i + PD < 4) prefetch(i + PD, in[(i + PD) % (PD + 1)]);
-#pragma clang loop unroll(full)
-        for (int q = 0; q < 4; ++q) {
-            const int64_t row = rbase + i * 32 + q * 8;
-            const bool rok = row < p.M;
-            float w[2][4];
-#pragma clang loop unroll(full)
-            for (int j = 0; j < 2; ++j) {
-                const float v[4] = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
-                quad_transpose(v, w[j], (jq & 1) != 0, (jq & 2) != 0);
-            }
+    // Whole tile inside M x N (and, for the split fp32 accumulate, on one side
+    // of nsplit): every operand is a uniform per-tile base plus this lane's
+    // fixed 32-bit offset plus a uniform per-(i, q, j) offset, so the accesses
+    // need no bounds checks and no per-element 64-bit index arithmetic.
+    bool fast = m0 + BM <= p.M && n0 + (p.swiglu ? BN / 2 : BN) <= p.N;
+    char* ob = nullptr;            // output tile base
+    int64_t old = e.ld0;           // its leading dimension (elements)
+    if constexpr (EPI == EPI_ACC_F32) {
+        if (n0 + BN <= e.nsplit) {
+            ob = static_cast<char*>(e.out0) + (m0 * e.ld0 + n0) * 4;
+        } else if (n0 >= e.nsplit) {
+            ob = static_cast<char*>(e.out1) + (m0 * e.ld1 + (n0 - e.nsplit)) * 4;
+            old = e.ld1;
+        } else {
+            fast = false;
+        }
+    } else {
+        ob = static_cast<char*>(e.out0) + (m0 * e.ld0 + n0) * ESO;
+    }
+    const uint32_t lo = (uint32_t)(((int64_t)lr * old + lc) * ESO);
+    const uint32_t li = (uint32_t)(((int64_t)lr * e.ldi0 + lc) * 2);
+    auto fptr = [&](int i, int q, int j) -> EpiPtr {
+        const int64_t uo = ((int64_t)(i * 32 + q * 8) * old + j * 32) * ESO;
+        EpiPtr a{};
+        char* o = ob + uo + lo;
+        a.o0 = o;
+        if constexpr (EPI == EPI_SWIGLU) {
+            a.o1 = static_cast<char*>(e.out1) + (m0 * e.ld0 + n0) * 2 + uo + lo;
+            a.o2 = static_cast<char*>(e.out2) + (m0 * e.ld0 + n0) * 2 + uo + lo;
+        } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+            a.o1 = o + e.nsplit * 2;
+            const int64_t ui = ((int64_t)(i * 32 + q * 8) * e.ldi0 + j * 32 + m0 * e.ldi0 + n0) * 2;
+            a.i0 = static_cast<const char*>(e.in0) + ui + li;
+            a.i1 = static_cast<const char*>(e.in1) + ui + li;
+        } else if constexpr (EPI == EPI_RESID) {
+            const int64_t ui = ((int64_t)(i * 32 + q * 8) * e.ldi0 + j * 32 + m0 * e.ldi0 + n0) * 2;
+            a.i0 = static_cast<const char*>(e.in0) + ui + li;
+        } else if constexpr (EPI == EPI_ACC_F32) {
+            a.i0 = o;
+        }
+        return a;
+    };
+    auto sptr = [&](int64_t row, int64_t col) -> EpiPtr {
+        EpiPtr a{};
+        if constexpr (EPI == EPI_ACC_F32) {
+            float* c = acc_ptr(e, row, col);
+            a.o0 = reinterpret_cast<char*>(c);
+            a.i0 = reinterpret_cast<const char*>(c);
+        } else {
+            a.o0 = static_cast<char*>(e.out0) + (row * e.ld0 + col) * ESO;
             if constexpr (EPI == EPI_SWIGLU) {
-                // a wavefront's 64 B rows are 32 gate rows then 32 up rows of the
-                // same 32 hidden columns
-                const int64_t col = n0 + wn * 32 + cq;
-                if (rok && col < p.N) epi4_swiglu(p.e, row, col, w[0], w[1]);
-            } else {
+                a.o1 = static_cast<char*>(e.out1) + (row * e.ld0 + col) * 2;
+                a.o2 = static_cast<char*>(e.out2) + (row * e.ld0 + col) * 2;
+            } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+                a.o1 = a.o0 + e.nsplit * 2;
+                a.i0 = static_cast<const char*>(e.in0) + (row * e.ldi0 + col) * 2;
+                a.i1 = static_cast<const char*>(e.in1) + (row * e.ldi0 + col) * 2;
+            } else if constexpr (EPI == EPI_RESID) {
+                a.i0 = static_cast<const char*>(e.in0) + (row * e.ldi0 + col) * 2;
+            }
+        }
+        return a;
+    };
+
+    auto run = [&](auto fast_c) {
+        constexpr bool FAST = decltype(fast_c)::value;
+        auto ptr = [&](int i, int q, int j) -> EpiPtr {
+            if constexpr (FAST) return fptr(i, q, j);
+            else return sptr(m0 + lr + i * 32 + q * 8, n0 + lc + j * 32);
+        };
+        auto ok = [&](int i, int q, int j) -> bool {
+            if constexpr (FAST) return true;
+            else return m0 + lr + i * 32 + q * 8 < p.M && n0 + lc + j * 32 < p.N;
+        };
+        auto prefetch = [&](int i, EpiIn<EPI> (&dst)[4][2]) {
+            if constexpr (HAS_IN) {
+#pragma clang loop unroll(full)
+                for (int q = 0; q < 4; ++q)
+#pragma clang loop unroll(full)
+                    for (int j = 0; j < 2; ++j)
+                        if (ok(i, q, j)) epi_load<EPI>(ptr(i, q, j), dst[q][j]);
+            }
+        };
+#pragma clang loop unroll(full)
+        for (int i = 0; i < PD; ++i) prefetch(i, in[i]);
+#pragma clang loop unroll(full)
+        for (int i = 0; i < 4; ++i) {
+            if (i + PD < 4) prefetch(i + PD, in[(i + PD) % (PD + 1)]);
+#pragma clang loop unroll(full)
+            for (int q = 0; q < 4; ++q) {
+                float w[2][4];
 #pragma clang loop unroll(full)
                 for (int j = 0; j < 2; ++j) {
-                    const int64_t col = n0 + wn * 64 + j * 32 + cq;
-                    if (rok && col < p.N) epi4<EPI>(p.e, row, col, w[j], in[i % (PD + 1)][q][j]);
+                    const float v[4] = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
+                    quad_transpose(v, w[j], (jq & 1) != 0, (jq & 2) != 0);
+                }
+                if constexpr (EPI == EPI_SWIGLU) {
+                    // a wavefront's 64 B rows are 32 gate rows then 32 up rows
+                    // of the same 32 hidden columns
+                    if (ok(i, q, 0)) epi4_swiglu(ptr(i, q, 0), w[0], w[1]);
+                } else {
+#pragma clang loop unroll(full)
+                    for (int j = 0; j < 2; ++j)
+                        if (ok(i, q, j)) epi4<EPI>(ptr(i, q, j), w[j], in[i % (PD + 1)][q][j]);
                 }
             }
         }
-    }
+    };
+    if (fast) run(std::true_type{});
+    else run(std::false_type{});
 }
 
 // Byte extent of a row-major operand: (rows-1)*ld + cols elements of bf16.
