@@ -55,31 +55,41 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
     return s;
 }
 
-// One workgroup per row.
-template <typename S>
+// One workgroup per row; the row stays in registers between the sum of
+// squares and the scaling (each thread holds Q chunks of 8 elements).
+template <typename S, int Q>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const S* __restrict__ x, const float* __restrict__ gamma,
                                                           float eps, int64_t d, float* __restrict__ r,
                                                           S* __restrict__ n, S* __restrict__ xcopy) {
     __shared__ float red[4];
     const int64_t row = blockIdx.x;
+    const int64_t nchunk = d / 8;
     const S* xr = x + row * d;
+    float v[Q][8];
     float ss = 0.0f;
-    for (int64_t c = (int64_t)threadIdx.x * 8; c < d; c += 256 * 8) {
-        float v[8];
-        Vec8<S>::load(xr + c, v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ss += v[i] * v[i];
+    for (int q = 0; q < Q; ++q) {
+        const int64_t c = threadIdx.x + 256 * q;
+        if (c < nchunk) {
+            Vec8<S>::load(xr + c * 8, v[q]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss += v[q][i] * v[q][i];
+        }
     }
     ss = block_sum(ss, red);
     const float rr = 1.0f / sqrtf(ss / (float)d + eps);
     if (threadIdx.x == 0) r[row] = rr;
-    for (int64_t c = (int64_t)threadIdx.x * 8; c < d; c += 256 * 8) {
-        float v[8], o[8];
-        Vec8<S>::load(xr + c, v);
-        if (xcopy) Vec8<S>::store(xcopy + row * d + c, v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = (v[i] * rr) * gamma[c + i];
-        Vec8<S>::store(n + row * d + c, o);
+    for (int q = 0; q < Q; ++q) {
+        const int64_t c = threadIdx.x + 256 * q;
+        if (c < nchunk) {
+            float gm[8], o[8];
+            Vec8<float>::load(gamma + c * 8, gm);
+            if (xcopy) Vec8<S>::store(xcopy + row * d + c * 8, v[q]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = (v[q][i] * rr) * gm[i];
+            Vec8<S>::store(n + row * d + c * 8, o);
+        }
     }
 }
 
@@ -109,7 +119,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
         const int64_t row = r0 + rr;
         if (row >= T) break;
         const float rv = r[row];
-        float a[Q][8], xv[Q][8];
+        float a[Q][8], xv[Q][8], dyv[Q][8];
         float dot = 0.0f;
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
@@ -118,6 +128,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
                 float dnv[8];
                 Vec8<float>::load(dn + row * d + c * 8, dnv);
                 Vec8<S>::load(x + row * d + c * 8, xv[q]);
+                Vec8<S>::load(dy + row * d + c * 8, dyv[q]);   // issued before the reduction
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     a[q][i] = dnv[i] * gam[q][i];
@@ -132,10 +143,9 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
         for (int q = 0; q < Q; ++q) {
             const int64_t c = threadIdx.x + 256 * q;
             if (c < nchunk) {
-                float dyv[8], o[8];
-                Vec8<S>::load(dy + row * d + c * 8, dyv);
+                float o[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) o[i] = dyv[i] + rv * a[q][i] - coef * xv[q][i];
+                for (int i = 0; i < 8; ++i) o[i] = dyv[q][i] + rv * a[q][i] - coef * xv[q][i];
                 Vec8<S>::store(dx + row * d + c * 8, o);
             }
         }
@@ -301,14 +311,18 @@ inline unsigned grid_for(int64_t work, int64_t per_block = 256, int64_t cap = 1 
 hipError_t rmsnorm_fwd(int dtype, const void* x, const float* gamma, float eps, int64_t T, int64_t d, float* r,
                        void* n, void* xcopy, hipStream_t s) {
     if (T <= 0) return hipSuccess;
-    if (dtype == PPS_DTYPE_BF16)
-        hipLaunchKernelGGL(rmsnorm_fwd_kernel<uint16_t>, dim3((unsigned)T), dim3(256), 0, s,
-                           static_cast<const uint16_t*>(x), gamma, eps, d, r, static_cast<uint16_t*>(n),
-                           static_cast<uint16_t*>(xcopy));
-    else
-        hipLaunchKernelGGL(rmsnorm_fwd_kernel<float>, dim3((unsigned)T), dim3(256), 0, s,
-                           static_cast<const float*>(x), gamma, eps, d, r, static_cast<float*>(n),
-                           static_cast<float*>(xcopy));
+    const int64_t q = (d / 8 + 255) / 256;   // chunks of 8 per thread
+#define PPS_RF(S, Q)                                                                                       \
+    hipLaunchKernelGGL((rmsnorm_fwd_kernel<S, Q>), dim3((unsigned)T), dim3(256), 0, s, static_cast<const S*>(x), \
+                       gamma, eps, d, r, static_cast<S*>(n), static_cast<S*>(xcopy))
+    if (dtype == PPS_DTYPE_BF16) {
+        if (q <= 1) PPS_RF(uint16_t, 1); else if (q <= 2) PPS_RF(uint16_t, 2); else if (q <= 4) PPS_RF(uint16_t, 4);
+        else if (q <= 8) PPS_RF(uint16_t, 8); else return hipErrorInvalidValue;
+    } else {
+        if (q <= 1) PPS_RF(float, 1); else if (q <= 2) PPS_RF(float, 2); else if (q <= 4) PPS_RF(float, 4);
+        else if (q <= 8) PPS_RF(float, 8); else return hipErrorInvalidValue;
+    }
+#undef PPS_RF
     return hipGetLastError();
 }
 
