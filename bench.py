@@ -36,10 +36,10 @@ PEAK_HBM_GBS = 8000.0
 # copy kernel measured in the same runs).  Valid only for the GEMM source they were taken on.
 TRAFFIC = {
     "config": "c3_80layer_p8_stage0",
-    "gemm_source_sha1": "20cfdcab728f7710c5e2c665b442bb2adbe27179",
+    "gemm_source_sha1": "ec0dcce777dfeafeaac508bc064065b545bcd60c",
     "bytes_per_launch": {
-        "gemm_gateup_swiglu": 13.078e9, "gemm_down_residual": 5.908e9, "gemm_dh_swiglu_bwd": 7.539e9,
-        "gemm_dn": 11.585e9, "gemm_wgrad_down": 7.519e9, "gemm_wgrad_gateup": 15.205e9,
+        "gemm_gateup_swiglu": 13.02e9, "gemm_down_residual": 5.912e9, "gemm_dh_swiglu_bwd": 7.626e9,
+        "gemm_dn": 11.61e9, "gemm_wgrad_down": 7.518e9, "gemm_wgrad_gateup": 15.09e9,
     },
 }
 
