@@ -96,12 +96,15 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const S* __restrict__ 
 constexpr int BWD_ROWS = 16;   // rows per workgroup in the RMSNorm backward
 
 // a = dn gamma; dx = dy + r a - r^3 x (a.x)/d; dgamma partial of the
-// workgroup's rows = sum dn x r (kept in registers, written once).
+// workgroup's rows = sum dn x r (kept in registers, written once).  With n,
+// also writes the block's RMSNorm output n = (x r) gamma again, computed as
+// the forward computed it (same bits), for the weight gradients.
 template <typename S, int Q>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restrict__ dn, const S* __restrict__ x,
                                                           const float* __restrict__ r, const float* __restrict__ gamma,
                                                           const S* __restrict__ dy, int64_t T, int64_t d,
-                                                          S* __restrict__ dx, float* __restrict__ partial) {
+                                                          S* __restrict__ dx, float* __restrict__ partial,
+                                                          S* __restrict__ n) {
     __shared__ float red[4];
     const int64_t nchunk = d / 8;
     float gam[Q][8], gp[Q][8];
@@ -147,6 +150,11 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
 #pragma unroll
                 for (int i = 0; i < 8; ++i) o[i] = dyv[q][i] + rv * a[q][i] - coef * xv[q][i];
                 Vec8<S>::store(dx + row * d + c * 8, o);
+                if (n) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) o[i] = (xv[q][i] * rv) * gam[q][i];
+                    Vec8<S>::store(n + row * d + c * 8, o);
+                }
             }
         }
     }
@@ -221,19 +229,14 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ a
     out[j] += s;
 }
 
-// 64 x 64 tile transposes through LDS.  Source rows r < rows, columns
-// c < cols (cols % 8 == 0); destination row map(c), column r, stride ldd
-// (ldd % 8 == 0); destination columns in [rows, ldd) are written as zero.
+// 64 x 64 tile transposes of bf16 through LDS.  Source rows r < rows,
+// columns c < cols (cols % 8 == 0); destination row map(c), column r, stride
+// ldd (ldd % 8 == 0); destination columns in [rows, ldd) are written as zero.
 // map(c) = c, or with grp > 0: (c / grp) * 2 grp + half * grp + c % grp
 // (gate/up interleave of the forward weight copy).
-//   MODE 0: dst = src
-//   MODE 1: dst = (src * r[row]) * gamma[col]        (RMSNorm output n)
-//   MODE 2: dst = silu(src) * src2                    (SwiGLU output h)
-template <typename S, int MODE>
-__global__ __launch_bounds__(256) void tile_transpose_kernel(const S* __restrict__ src, const S* __restrict__ src2,
-                                                             const float* __restrict__ r, const float* __restrict__ gamma,
-                                                             int64_t rows, int64_t cols, int64_t lds, S* __restrict__ dst,
-                                                             int64_t ldd, int grp, int half) {
+__global__ __launch_bounds__(256) void tile_transpose_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
+                                                             int64_t lds, uint16_t* __restrict__ dst, int64_t ldd,
+                                                             int grp, int half) {
     __shared__ float tile[64][65];
     const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
     const int t = threadIdx.x;
@@ -243,17 +246,7 @@ __global__ __launch_bounds__(256) void tile_transpose_kernel(const S* __restrict
         const int64_t row = r0 + rr, col = c0 + c8;
         float v[8];
         if (row < rows && col < cols) {
-            Vec8<S>::load(src + row * lds + col, v);
-            if constexpr (MODE == 1) {
-                const float rv = r[row];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) v[j] = (v[j] * rv) * gamma[col + j];
-            } else if constexpr (MODE == 2) {
-                float u[8];
-                Vec8<S>::load(src2 + row * lds + col, u);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) v[j] = swiglu_f(v[j], u[j]);
-            }
+            Vec8<uint16_t>::load(src + row * lds + col, v);
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] = 0.0f;
@@ -271,7 +264,7 @@ __global__ __launch_bounds__(256) void tile_transpose_kernel(const S* __restrict
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] = tile[r8 + j][cc];
             const int64_t drow = grp ? (col / grp) * 2 * grp + (int64_t)half * grp + col % grp : col;
-            Vec8<S>::store(dst + drow * ldd + row, v);
+            Vec8<uint16_t>::store(dst + drow * ldd + row, v);
         }
     }
 }
@@ -330,27 +323,28 @@ int rmsnorm_bwd_partial_rows(int64_t T) { return (int)((T + BWD_ROWS - 1) / BWD_
 
 template <typename S>
 static hipError_t rmsnorm_bwd_t(const float* dn, const void* x, const float* r, const float* gamma, const void* dy,
-                                int64_t T, int64_t d, void* dx, float* partial, hipStream_t s) {
+                                int64_t T, int64_t d, void* dx, float* partial, void* n, hipStream_t s) {
     const int64_t q = (d / 8 + 255) / 256;
     const dim3 grid((unsigned)rmsnorm_bwd_partial_rows(T));
     const S* xs = static_cast<const S*>(x);
     const S* dys = static_cast<const S*>(dy);
     S* dxs = static_cast<S*>(dx);
-    if (q <= 1) hipLaunchKernelGGL((rmsnorm_bwd_kernel<S, 1>), grid, dim3(256), 0, s, dn, xs, r, gamma, dys, T, d, dxs, partial);
-    else if (q <= 2) hipLaunchKernelGGL((rmsnorm_bwd_kernel<S, 2>), grid, dim3(256), 0, s, dn, xs, r, gamma, dys, T, d, dxs, partial);
-    else if (q <= 4) hipLaunchKernelGGL((rmsnorm_bwd_kernel<S, 4>), grid, dim3(256), 0, s, dn, xs, r, gamma, dys, T, d, dxs, partial);
-    else if (q <= 8) hipLaunchKernelGGL((rmsnorm_bwd_kernel<S, 8>), grid, dim3(256), 0, s, dn, xs, r, gamma, dys, T, d, dxs, partial);
+    S* ns = static_cast<S*>(n);
+    if (q <= 1) hipLaunchKernelGGL((rmsnorm_bwd_kernel<S, 1>), grid, dim3(256), 0, s, dn, xs, r, gamma, dys, T, d, dxs, partial, ns);
+    else if (q <= 2) hipLaunchKernelGGL((rmsnorm_bwd_kernel<S, 2>), grid, dim3(256), 0, s, dn, xs, r, gamma, dys, T, d, dxs, partial, ns);
+    else if (q <= 4) hipLaunchKernelGGL((rmsnorm_bwd_kernel<S, 4>), grid, dim3(256), 0, s, dn, xs, r, gamma, dys, T, d, dxs, partial, ns);
+    else if (q <= 8) hipLaunchKernelGGL((rmsnorm_bwd_kernel<S, 8>), grid, dim3(256), 0, s, dn, xs, r, gamma, dys, T, d, dxs, partial, ns);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 hipError_t rmsnorm_bwd(int dtype, const float* dn, const void* x, const float* r, const float* gamma, const void* dy,
-                       int64_t T, int64_t d, void* dx, float* partial, int* n_partial, hipStream_t s) {
+                       int64_t T, int64_t d, void* dx, float* partial, int* n_partial, void* n, hipStream_t s) {
     *n_partial = 0;
     if (T <= 0) return hipSuccess;
     *n_partial = rmsnorm_bwd_partial_rows(T);
-    return dtype == PPS_DTYPE_BF16 ? rmsnorm_bwd_t<uint16_t>(dn, x, r, gamma, dy, T, d, dx, partial, s)
-                                   : rmsnorm_bwd_t<float>(dn, x, r, gamma, dy, T, d, dx, partial, s);
+    return dtype == PPS_DTYPE_BF16 ? rmsnorm_bwd_t<uint16_t>(dn, x, r, gamma, dy, T, d, dx, partial, n, s)
+                                   : rmsnorm_bwd_t<float>(dn, x, r, gamma, dy, T, d, dx, partial, n, s);
 }
 
 hipError_t column_reduce_acc(const float* partial, int rows, int64_t d, float* out, hipStream_t s) {
@@ -387,20 +381,13 @@ hipError_t colsum_acc(const float* a, int64_t T, int64_t d, float* out, hipStrea
     return hipGetLastError();
 }
 
-hipError_t transpose(int dtype, int mode, const void* src, const void* src2, const float* r, const float* gamma,
-                     int64_t rows, int64_t cols, int64_t lds, void* dst, int64_t ldd, int grp, int half, hipStream_t s) {
+hipError_t transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t lds, void* dst, int64_t ldd, int grp,
+                          int half, hipStream_t s) {
     if (cols <= 0 || ldd <= 0) return hipSuccess;
     if (cols % 8 || ldd % 8 || lds % 8) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((ldd + 63) / 64), (unsigned)((cols + 63) / 64));
-#define PPS_TR(S, MODE)                                                                                          \
-    hipLaunchKernelGGL((tile_transpose_kernel<S, MODE>), grid, dim3(256), 0, s, static_cast<const S*>(src),        \
-                       static_cast<const S*>(src2), r, gamma, rows, cols, lds, static_cast<S*>(dst), ldd, grp, half)
-    if (dtype == PPS_DTYPE_BF16) {
-        if (mode == 0) PPS_TR(uint16_t, 0); else if (mode == 1) PPS_TR(uint16_t, 1); else PPS_TR(uint16_t, 2);
-    } else {
-        if (mode == 0) PPS_TR(float, 0); else if (mode == 1) PPS_TR(float, 1); else PPS_TR(float, 2);
-    }
-#undef PPS_TR
+    hipLaunchKernelGGL(tile_transpose_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), rows, cols, lds,
+                       static_cast<uint16_t*>(dst), ldd, grp, half);
     return hipGetLastError();
 }
 

@@ -29,6 +29,7 @@ __device__ __forceinline__ void epi_apply(const EpiArgs& e, int64_t row, int64_t
         S* o = static_cast<S*>(e.out0) + row * e.ld0;
         Store<S>::store(o + col, dg);
         Store<S>::store(o + e.nsplit + col, du);
+        if (e.out2) Store<S>::store(static_cast<S*>(e.out2) + row * e.ldi0 + col, swiglu_f(g, u));
     } else if constexpr (EPI == EPI_ACC_F32) {
         if (col < e.nsplit) static_cast<float*>(e.out0)[row * e.ld0 + col] += v;
         else static_cast<float*>(e.out1)[row * e.ld1 + (col - e.nsplit)] += v;

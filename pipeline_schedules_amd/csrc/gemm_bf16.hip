@@ -1,10 +1,12 @@
 // bf16 GEMM on the CDNA4 matrix cores (gfx950), fp32 accumulation.
 //
-// Layout: "TN" -- both operands K-contiguous: C[m,n] = sum_k A[m,k] B[n,k],
-// A row-major [M, K] (stride lda), B row-major [N, K] (stride ldb).  The
-// executor stores every operand so that the reduction dimension is
-// contiguous (transposed copies of weights and of the weight-gradient
-// activations), so this one kernel serves all six GEMMs of a SwiGLU block.
+// Layouts: C[m,n] = sum_k A(m,k) B(n,k) with both operands either
+//   K-contiguous ("TN"): A row-major [M, K] (stride lda), B [N, K] (ldb), or
+//   M/N-contiguous ("MN"): A row-major [K, M] (stride lda), B [K, N] (ldb).
+// The forward and input-gradient GEMMs run TN (the forward reads per-pass
+// K-contiguous copies of the weights); the weight-gradient GEMMs dW = X^T Y
+// reduce over tokens and read the activations and gradients as they are
+// stored, [T, features], in the MN mode, which needs no transposed copies.
 //
 // Tiling: macro-tile 256 x 256 x 64, 512 threads = 8 wavefronts in a 2 x 4
 // grid, 128 x 64 per wavefront = 4 x 2 tiles of v_mfma_f32_32x32x16_bf16
@@ -23,6 +25,16 @@
 // per bank period).  Buffer loads return zero outside the operand's extent,
 // which pads ragged M, N and K tails without branches.
 //
+// MN mode: an operand tile is 64 k-rows of 256 M (or N) values, 512 bytes
+// each; 16-byte chunk c of k-row k sits at position c ^ (4 * (k & 3)).  Each
+// load instruction moves two k-rows.  MFMA fragments, which hold 8
+// consecutive k per lane, come from two ds_read_b64_tr_b16 each (the LDS
+// transposes 4 x 4 blocks of 16-bit values across lanes on the way out); the
+// swizzle keeps both the loads' writes and these reads free of bank
+// conflicts.  Twice the LDS read instructions of the TN mode for the same
+// bytes; the per-lane read addresses are fixed, with the K sub-step and the
+// slot in the immediate offset and one scalar base.
+//
 // Workgroup -> tile mapping: the dispatcher places workgroup i on XCD i % 8;
 // ids are remapped so each XCD gets a contiguous run of logical tiles, and
 // logical tiles are ordered in groups of 8 tile-rows so the tiles running on
@@ -35,6 +47,8 @@ namespace pps {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 #define LDS_AS __attribute__((address_space(3)))
@@ -174,6 +188,12 @@ __device__ __forceinline__ void epi4(const EpiPtr& a, const float (&w)[4], const
         for (int k = 0; k < 4; ++k) swiglu_bwd_f(w[k], g[k], u[k], dg[k], du[k]);
         *reinterpret_cast<uint2*>(a.o0) = pack4(dg);
         *reinterpret_cast<uint2*>(a.o1) = pack4(du);
+        if (a.o2) {   // optional h = silu(g) u, as the forward computed it
+            float hh[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) hh[k] = swiglu_f(g[k], u[k]);
+            *reinterpret_cast<uint2*>(a.o2) = pack4(hh);
+        }
     } else if constexpr (EPI == EPI_ACC_F32) {
         const float4 c = in.c;
         *reinterpret_cast<float4*>(a.o0) = make_float4(c.x + w[0], c.y + w[1], c.z + w[2], c.w + w[3]);
@@ -200,7 +220,17 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
-template <int EPI>
+// Direct-to-LDS load of 16 bytes per lane (to LDS address lds + 16 * lane)
+// issued from inline assembly: for the builtin form the compiler makes every
+// later transposing LDS read wait for all loads in flight (it cannot tell
+// that they touch other slots).  The explicit vmcnt waits of the K loop order
+// these loads.  Kernels that use it set M0 nowhere else.
+__device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
+
+template <int EPI, bool MN>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
@@ -221,7 +251,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     int lcq[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) lcq[q] = (lane & 7) ^ (((wave * 4 + q) * 4 + (lane >> 4)) & 7);
+    // MN mode: piece q holds k-rows kq[q] = (wave*4+q)*2 + l/32, lane l the
+    // LDS chunk l&31 = logical chunk (l&31) ^ 4*(kq[q]&3); the K step (64
+    // k-rows) rides in soffset.
+    int kq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kq[q] = (wave * 4 + q) * 2 + (lane >> 5);
+    auto mn_off = [&](int q, int64_t col0, int64_t ncols, int64_t ld) -> uint32_t {
+        const int64_t col = col0 + (((lane & 31) ^ (4 * (kq[q] & 3))) * 8);
+        return col < ncols ? (uint32_t)((kq[q] * ld + col) * 2) : OOB;
+    };
     uint32_t aoff[4], boff[4];
+    uint32_t astep = BK * 2, bstep = BK * 2;   // bytes per K step
     rsrc_t ar, br;
     int64_t K = 0;
     auto set_seg = [&](int s) {
@@ -229,12 +270,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         ar = make_rsrc(g.A, g.a_bytes);
         br = make_rsrc(g.B, g.b_bytes);
         K = g.K;
+        if constexpr (MN) {
+            astep = (uint32_t)(BK * g.lda * 2);
+            bstep = (uint32_t)(BK * g.ldb * 2);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int row = (wave * 4 + q) * 8 + lrow;
-            const int64_t ra = m0 + row, rb = nb0 + row;
-            aoff[q] = ra < p.M ? (uint32_t)(ra * g.lda * 2 + lcq[q] * 16) : OOB;
-            boff[q] = rb < p.NB ? (uint32_t)(rb * g.ldb * 2 + lcq[q] * 16) : OOB;
+            if constexpr (MN) {
+                aoff[q] = mn_off(q, m0, p.M, g.lda);
+                boff[q] = mn_off(q, nb0, p.NB, g.ldb);
+            } else {
+                const int row = (wave * 4 + q) * 8 + lrow;
+                const int64_t ra = m0 + row, rb = nb0 + row;
+                aoff[q] = ra < p.M ? (uint32_t)(ra * g.lda * 2 + lcq[q] * 16) : OOB;
+                boff[q] = rb < p.NB ? (uint32_t)(rb * g.ldb * 2 + lcq[q] * 16) : OOB;
+            }
         }
     };
     // Piece q of K tile kt (past the segment's K: zeros).  Branch-free, so the
@@ -243,31 +293,75 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         const int64_t rem = K - (int64_t)kt * BK;
         return rem <= 0 ? 0 : rem >= BK ? BK / 8 : (int)rem / 8;   // valid 16-byte chunks per row
     };
+    // In K range: TN pieces hold 16-byte K chunks, MN pieces whole k-rows.
+    auto kin = [&](int kt, int q) {
+        if constexpr (MN) return kq[q] < (int)(K - (int64_t)kt * BK);
+        else return lcq[q] < chunks_left(kt);
+    };
+    const uint32_t lds0 = (uint32_t)(size_t)(LDS_AS char*)smem;
     auto issueA = [&](int kt, int q) {
-        char* st = smem + (kt % ASLOTS) * OPB;
-        const uint32_t ao = lcq[q] < chunks_left(kt) ? aoff[q] : OOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (LDS_AS void*)(st + (wave_s * 4 + q) * 1024), 16, ao,
-                                                 (uint32_t)kt * (BK * 2), 0, 0);
+        const int so = (kt % ASLOTS) * OPB + (wave_s * 4 + q) * 1024;
+        const uint32_t ao = kin(kt, q) ? aoff[q] : OOB;
+        if constexpr (MN)
+            lds_load16(ar, lds0 + so, ao, (uint32_t)kt * astep);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (LDS_AS void*)(smem + so), 16, ao, (uint32_t)kt * astep, 0, 0);
     };
     auto issueB = [&](int kt, int q) {
-        char* st = smem + BBASE + (kt & 1) * OPB;
-        const uint32_t bo = lcq[q] < chunks_left(kt) ? boff[q] : OOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (LDS_AS void*)(st + (wave_s * 4 + q) * 1024), 16, bo,
-                                                 (uint32_t)kt * (BK * 2), 0, 0);
+        const int so = BBASE + (kt & 1) * OPB + (wave_s * 4 + q) * 1024;
+        const uint32_t bo = kin(kt, q) ? boff[q] : OOB;
+        if constexpr (MN)
+            lds_load16(br, lds0 + so, bo, (uint32_t)kt * bstep);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (LDS_AS void*)(smem + so), 16, bo, (uint32_t)kt * bstep, 0, 0);
     };
 
     // MFMA operand fragment: row r, logical chunk ch at r*128 + (ch ^ ((r>>1)&7))*16.
     const int fsw = ((lane & 31) >> 1) & 7;
+    // MN fragment of the 32 columns at cb, k = 16*kk .. +15: in 16-lane group
+    // g = l/16, lane s = l%16 addresses k-row 16*kk + 8*(g>>1) + s/4 (+4 for
+    // the second read) at columns cb + 16*(g&1) + 4*(s&3) .. +3, and lane j of
+    // the group receives column cb + 16*(g&1) + j of four consecutive k-rows,
+    // which is the MFMA layout (lane l: column l%32, k = 8*(l/32) .. +7).  The
+    // k-row's low two bits are s/4 for every kk, so the swizzle, and with it
+    // the whole per-lane offset, is fixed.
+    const int tg = lane >> 4, ts = lane & 15;
+    auto mn_lane_off = [&](int cb) -> int {
+        const int ch = ((cb >> 3) + 2 * (tg & 1) + ((ts & 3) >> 1)) ^ (4 * (ts >> 2));
+        return (8 * (tg >> 1) + (ts >> 2)) * 512 + (ch << 4) + ((ts & 1) << 3);
+    };
+    int mn_aoff[4], mn_boff[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mn_aoff[i] = mn_lane_off(wm * 128 + i * 32);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) mn_boff[j] = mn_lane_off(wn * 64 + j * 32);
+    auto mn_frag = [&](uint32_t base, int loff, int kk) -> bf16x8 {
+        LDS_AS char* q = (LDS_AS char*)(size_t)(base + (uint32_t)loff);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(q + kk * 8192));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(q + kk * 8192 + 2048));
+        const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    };
     auto frags = [&](int kt, int kk, bf16x8 (&a)[4], bf16x8 (&b)[2]) {
-        const char* sa = smem + (kt % ASLOTS) * OPB;
-        const char* sb = smem + BBASE + (kt & 1) * OPB;
-        const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) << 4;
+        if constexpr (MN) {
+            // slot bases as scalars, so the per-read offsets stay immediates
+            const uint32_t ua = __builtin_amdgcn_readfirstlane(lds0 + (kt % ASLOTS) * OPB);
+            const uint32_t ub = __builtin_amdgcn_readfirstlane(lds0 + BBASE + (kt & 1) * OPB);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32 + (lane & 31)) * ROWB + pc);
+            for (int i = 0; i < 4; ++i) a[i] = mn_frag(ua, mn_aoff[i], kk);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            b[j] = *reinterpret_cast<const bf16x8*>(sb + (wn * 64 + j * 32 + (lane & 31)) * ROWB + pc);
+            for (int j = 0; j < 2; ++j) b[j] = mn_frag(ub, mn_boff[j], kk);
+        } else {
+            const char* sa = smem + (kt % ASLOTS) * OPB;
+            const char* sb = smem + BBASE + (kt & 1) * OPB;
+            const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) << 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32 + (lane & 31)) * ROWB + pc);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[j] = *reinterpret_cast<const bf16x8*>(sb + (wn * 64 + j * 32 + (lane & 31)) * ROWB + pc);
+        }
     };
 
     f32x16 acc[4][2];
@@ -368,6 +462,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
             const int64_t ui = ((int64_t)(i * 32 + q * 8) * e.ldi0 + j * 32 + m0 * e.ldi0 + n0) * 2;
             a.i0 = static_cast<const char*>(e.in0) + ui + li;
             a.i1 = static_cast<const char*>(e.in1) + ui + li;
+            a.o2 = e.out2 ? static_cast<char*>(e.out2) + ui + li : nullptr;
         } else if constexpr (EPI == EPI_RESID) {
             const int64_t ui = ((int64_t)(i * 32 + q * 8) * e.ldi0 + j * 32 + m0 * e.ldi0 + n0) * 2;
             a.i0 = static_cast<const char*>(e.in0) + ui + li;
@@ -391,6 +486,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
                 a.o1 = a.o0 + e.nsplit * 2;
                 a.i0 = static_cast<const char*>(e.in0) + (row * e.ldi0 + col) * 2;
                 a.i1 = static_cast<const char*>(e.in1) + (row * e.ldi0 + col) * 2;
+                a.o2 = e.out2 ? static_cast<char*>(e.out2) + (row * e.ldi0 + col) * 2 : nullptr;
             } else if constexpr (EPI == EPI_RESID) {
                 a.i0 = static_cast<const char*>(e.in0) + (row * e.ldi0 + col) * 2;
             }
@@ -454,9 +550,9 @@ inline bool extent(int64_t rows, int64_t ld, int64_t cols, uint32_t& out) {
     return true;
 }
 
-template <int EPI>
+template <int EPI, bool MN = false>
 hipError_t launch(const Params& p, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_tn_kernel<EPI>), dim3(p.tiles_m * p.tiles_n), dim3(NTHREADS), 0, s, p);
+    hipLaunchKernelGGL((gemm_tn_kernel<EPI, MN>), dim3(p.tiles_m * p.tiles_n), dim3(NTHREADS), 0, s, p);
     return hipGetLastError();
 }
 
@@ -464,12 +560,15 @@ hipError_t launch(const Params& p, hipStream_t s) {
 
 int64_t swiglu_b_rows(int64_t ffn) { return 2 * ((ffn + 31) / 32) * 32; }
 
-// Requires K-contiguous A and B, 16-byte aligned rows, every operand extent
-// under 2 GB.  With the SwiGLU map, B is the gate/up weight interleaved per 32
-// hidden columns (32 gate rows, then 32 up rows; swiglu_b_rows(N) rows) and N
-// is the number of hidden columns.
+// Requires A and B both K-contiguous, or both M/N-contiguous (then only with
+// the fp32 store or accumulate epilogue), 16-byte aligned rows, every operand
+// extent under 2 GB.  With the SwiGLU map, B is the gate/up weight
+// interleaved per 32 hidden columns (32 gate rows, then 32 up rows;
+// swiglu_b_rows(N) rows) and N is the number of hidden columns.
 hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
-    if (!a.a_kcontig || !a.b_kcontig) return hipErrorInvalidValue;
+    const bool mn = !a.a_kcontig;
+    if (a.b_kcontig == mn) return hipErrorInvalidValue;
+    if (mn && (a.swiglu_map || (a.epi != EPI_STORE_F32 && a.epi != EPI_ACC_F32))) return hipErrorInvalidValue;
     Params p{};
     p.M = a.M;
     p.N = a.N;
@@ -486,11 +585,15 @@ hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
         p.seg[i].lda = g.lda;
         p.seg[i].ldb = g.ldb;
         p.seg[i].K = g.K;
-        if (!extent(a.M, g.lda, g.K, p.seg[i].a_bytes) || !extent(p.NB, g.ldb, g.K, p.seg[i].b_bytes))
+        if (mn && (g.lda % 8 || g.ldb % 8 || (reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B)) % 16))
             return hipErrorInvalidValue;
+        const bool ok = mn ? extent(g.K, g.lda, a.M, p.seg[i].a_bytes) && extent(g.K, g.ldb, p.NB, p.seg[i].b_bytes)
+                           : extent(a.M, g.lda, g.K, p.seg[i].a_bytes) && extent(p.NB, g.ldb, g.K, p.seg[i].b_bytes);
+        if (!ok) return hipErrorInvalidValue;
     }
     p.e = a.e;
     if (p.tiles_m == 0 || p.tiles_n == 0) return hipSuccess;
+    if (mn) return a.epi == EPI_ACC_F32 ? launch<EPI_ACC_F32, true>(p, s) : launch<EPI_STORE_F32, true>(p, s);
     switch (a.epi) {
         case EPI_SWIGLU: return launch<EPI_SWIGLU>(p, s);
         case EPI_RESID: return launch<EPI_RESID>(p, s);

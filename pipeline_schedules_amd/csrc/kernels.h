@@ -19,7 +19,8 @@ enum Epi {
     EPI_STORE_F32 = 0,   // out0[m*ld0+n] = acc                           (float)
     EPI_RESID = 1,       // out0[m*ld0+n] = in0[m*ldi0+n] + acc           (storage type)
     EPI_SWIGLU = 2,      // g,u pair -> out0=g, out1=u, out2=h=silu(g)*u  (storage type, ld0)
-    EPI_SWIGLU_BWD = 3,  // dh=acc; g=in0,u=in1 (ldi0) -> out0[m*ld0+n]=dg, out0[..+nsplit]=du
+    EPI_SWIGLU_BWD = 3,  // dh=acc; g=in0,u=in1 (ldi0) -> out0[m*ld0+n]=dg, out0[..+nsplit]=du,
+                         // and if out2: out2[m*ldi0+n] = h = silu(g) u
     EPI_ACC_F32 = 4,     // n <  nsplit: out0[m*ld0+n] += acc; else out1[m*ld1+n-nsplit] += acc
     EPI_BIAS_GELU = 5,   // z = acc + bias[n]; out0 = z, out1 = GELU(z)   (fp32 only)
     EPI_STORE = 6,       // out0[m*ld0+n] = acc                           (storage type)
@@ -48,6 +49,8 @@ struct GemmArgs {
     int64_t M = 0, N = 0;       // output rows / columns (SwiGLU map: N = ffn)
     int nseg = 1;
     GemmSeg seg[2];
+    // bf16: both K-contiguous, or both M/N-contiguous (fp32 epilogues only);
+    // fp32: any combination.
     bool a_kcontig = true;
     bool b_kcontig = false;
     bool swiglu_map = false;    // B columns: per 2*H group, H from B then H from B2
@@ -65,9 +68,10 @@ hipError_t rmsnorm_fwd(int dtype, const void* x, const float* gamma, float eps,
 
 // a = dn gamma; dx = dy + r a - r^3 x (a.x)/d; partial[w, j] = sum over the
 // rows of workgroup w of dn x r.  Returns the number of partial rows used.
+// If n is given, also writes n = (x r) gamma [T, d] exactly as rmsnorm_fwd.
 hipError_t rmsnorm_bwd(int dtype, const float* dn, const void* x, const float* r,
                        const float* gamma, const void* dy, int64_t T, int64_t d,
-                       void* dx, float* partial, int* n_partial, hipStream_t s);
+                       void* dx, float* partial, int* n_partial, void* n, hipStream_t s);
 int rmsnorm_bwd_partial_rows(int64_t T);
 
 // out[j] += sum_{w < rows} partial[w, j]   (fixed order)
@@ -84,13 +88,12 @@ hipError_t gelu_bwd(const float* dy, const float* z, int64_t count, float* dz, h
 // out[j] += sum_t a[t, j]  (fp32, fixed order)
 hipError_t colsum_acc(const float* a, int64_t T, int64_t d, float* out, hipStream_t s);
 
-// Tiled transpose: dst[map(c), r] = f(src[r, c]) for r < rows, c < cols;
-// dst columns in [rows, ldd) are zeroed.  mode 0: copy; 1: (src r[row]) gamma[c];
-// 2: silu(src) src2.  map(c) = c, or (c/grp)*2grp + half*grp + c%grp with grp > 0.
-// cols, lds and ldd must be multiples of 8.
-hipError_t transpose(int dtype, int mode, const void* src, const void* src2, const float* r, const float* gamma,
-                     int64_t rows, int64_t cols, int64_t lds, void* dst, int64_t ldd, int grp, int half,
-                     hipStream_t s);
+// Tiled bf16 transpose: dst[map(c), r] = src[r, c] for r < rows, c < cols;
+// dst columns in [rows, ldd) are zeroed.  map(c) = c, or
+// (c/grp)*2grp + half*grp + c%grp with grp > 0.  cols, lds and ldd must be
+// multiples of 8.
+hipError_t transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t lds, void* dst, int64_t ldd, int grp,
+                          int half, hipStream_t s);
 
 // Rows of the interleaved gate/up weight copy used by the forward GEMM.
 int64_t swiglu_b_rows(int64_t ffn);

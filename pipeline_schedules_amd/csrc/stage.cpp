@@ -74,10 +74,7 @@ struct pps_stage {
     bool ac = false;
     size_t s_rc = 0;
     size_t s_n = 0, s_h = 0, s_dgu = 0, s_dn = 0, s_dxa = 0, s_dxb = 0, s_part = 0, s_dz = 0;
-    // bf16 path: K-contiguous operands of the weight-gradient GEMMs ([feature, Tp])
-    size_t s_nT = 0, s_hT = 0, s_dguT = 0, s_dyT = 0;
-    int64_t Tp = 0;                   // T rounded up to a multiple of 8
-    bool tn = false;                  // bf16 path: every GEMM runs with K-contiguous operands
+    bool tn = false;                  // bf16 path: the forward GEMMs read K-contiguous weight copies
     // bf16 path: per-pass copies of the forward weights, [chunk*L + block]:
     // WguT (swiglu_b_rows(ffn) x d, gate/up interleaved per 32) and WdT (d x ffn)
     char* wcopy = nullptr;
@@ -142,9 +139,9 @@ hipError_t timed(pps_stage* h, int kernel, double flops, double bytes, F&& launc
         }                                      \
     } while (0)
 
-// With tn (bf16 path) the split extras are the transposed dg|du [2 ffn, Tp]
-// and dy [d, Tp] that the deferred weight-gradient GEMMs read.
-Layout make_layout(const pps_stage_desc& d, bool swiglu, bool split, int es, bool tn, int64_t Tp) {
+// With the split, each block also keeps dg|du [T, 2 ffn] and dy [T, d] for
+// the deferred weight-gradient GEMMs.
+Layout make_layout(const pps_stage_desc& d, bool swiglu, bool split, int es) {
     Layout L;
     const size_t T = (size_t)d.T, dm = (size_t)d.d, f = (size_t)d.ffn;
     size_t off = 0;
@@ -165,8 +162,8 @@ Layout make_layout(const pps_stage_desc& d, bool swiglu, bool split, int es, boo
     if (split) {
         for (int b = 0; b < nb; ++b) {
             if (swiglu) {
-                take(L.dgu, (tn ? (size_t)Tp : T) * 2 * f * es);
-                take(L.dy, (tn ? (size_t)Tp : T) * dm * es);
+                take(L.dgu, T * 2 * f * es);
+                take(L.dy, T * dm * es);
             } else {
                 take(L.dz, T * dm * 4);
             }
@@ -190,11 +187,11 @@ int validate_desc(const pps_stage_desc* d) {
     if (!(d->eps >= 0.0f)) return PPS_EINVAL;
     if (d->block_type == PPS_BLOCK_SWIGLU && d->dtype == PPS_DTYPE_BF16) {
         // The MFMA GEMM addresses each operand with 32-bit byte offsets: the
-        // largest ones (dg|du [T, 2 ffn], its transposed copy, the interleaved
-        // gate/up weight copy) must stay under 2 GiB.
-        const double lim = 2147483648.0, T = (double)d->T, Tp = (double)((d->T + 7) / 8 * 8);
+        // largest ones (dg|du [T, 2 ffn], the interleaved gate/up weight copy)
+        // must stay under 2 GiB.
+        const double lim = 2147483648.0, T = (double)d->T;
         const double f2 = 2.0 * (double)d->ffn, rows = (double)pps::swiglu_b_rows(d->ffn);
-        if (T * f2 * 2 >= lim || Tp * f2 * 2 >= lim || rows * (double)d->d * 2 >= lim) return PPS_EINVAL;
+        if (T * f2 * 2 >= lim || rows * (double)d->d * 2 >= lim) return PPS_EINVAL;
     }
     if ((d->flags & PPS_FLAG_PROFILE) && d->profile_capacity < 0) return PPS_EINVAL;
     if (!(d->flags & PPS_FLAG_BOOKKEEPING_ONLY)) {
@@ -256,12 +253,12 @@ int refresh_weight_copies(pps_stage* h) {
         char* wgu = h->wcopy + h->wgu_off[i];
         char* wdt = h->wcopy + h->wd_off[i];
         PPS_TRY(timed(h, PPS_K_COPY, 0.0, 4.0 * d * f * 2, [&] {
-            hipError_t e = pps::transpose(D.dtype, 0, wb[0], nullptr, nullptr, nullptr, d, f, f, wgu, d, 32, 0, h->stream);
-            if (e == hipSuccess) e = pps::transpose(D.dtype, 0, wb[1], nullptr, nullptr, nullptr, d, f, f, wgu, d, 32, 1, h->stream);
+            hipError_t e = pps::transpose_bf16(wb[0], d, f, f, wgu, d, 32, 0, h->stream);
+            if (e == hipSuccess) e = pps::transpose_bf16(wb[1], d, f, f, wgu, d, 32, 1, h->stream);
             return e;
         }));
         PPS_TRY(timed(h, PPS_K_COPY, 0.0, 2.0 * d * f * 2, [&] {
-            return pps::transpose(D.dtype, 0, wb[2], nullptr, nullptr, nullptr, f, d, d, wdt, f, 0, 0, h->stream);
+            return pps::transpose_bf16(wb[2], f, d, d, wdt, f, 0, 0, h->stream);
         }));
     }
     return PPS_OK;
@@ -324,26 +321,13 @@ int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_
     return PPS_OK;
 }
 
-// bf16 path: write the transposed dy [d, Tp] and dg|du [2 ffn, Tp] that the
-// weight-gradient GEMMs read with K = T contiguous.
-int swiglu_stage_w_operands(pps_stage* h, const void* dy, const void* dgu, void* dyT, void* dguT) {
+// Weight gradient of block b: dWd += h^T dy; dWg += n^T dg; dWu += n^T du.
+// Every operand is read as stored, [T, features] (the GEMMs reduce over the
+// T rows).  n and h are in the scratch buffers when `have_nh` (the backward
+// just produced them); otherwise they are recomputed from the stash.
+int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, const void* dgu, bool have_nh) {
     const pps_stage_desc& D = h->d;
-    const int64_t T = D.T, d = D.d, f = D.ffn, Tp = h->Tp;
-    PPS_TRY(timed(h, PPS_K_COPY, 0.0, (double)(T + Tp) * d * 2, [&] {
-        return pps::transpose(D.dtype, 0, dy, nullptr, nullptr, nullptr, T, d, d, dyT, Tp, 0, 0, h->stream);
-    }));
-    PPS_TRY(timed(h, PPS_K_COPY, 0.0, (double)(T + Tp) * 2 * f * 2, [&] {
-        return pps::transpose(D.dtype, 0, dgu, nullptr, nullptr, nullptr, T, 2 * f, 2 * f, dguT, Tp, 0, 0, h->stream);
-    }));
-    return PPS_OK;
-}
-
-// Weight gradient of block b: dWd += h^T dy; dWg += n^T dg; dWu += n^T du,
-// with n and h recomputed from the stash.  bf16 path: dy and dgu are the
-// transposed [d, Tp] and [2 ffn, Tp] copies; fp32 path: row-major [T, .].
-int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, const void* dgu) {
-    const pps_stage_desc& D = h->d;
-    const int64_t T = D.T, d = D.d, f = D.ffn, Tp = h->Tp;
+    const int64_t T = D.T, d = D.d, f = D.ffn;
     const int dt = D.dtype, es = h->es;
     const void* const* wb = h->w.data() + (size_t)(chunk * D.L + b) * 4;
     const float* gamma = static_cast<const float*>(wb[3]);
@@ -352,38 +336,25 @@ int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, cons
     float* dWu = h->grads + h->goff[gi + 1];
     float* dWd = h->grads + h->goff[gi + 2];
     char* ab = acts(h, slot);
-    const char* xb = act_x(h, slot, b);
-    const float* rb = reinterpret_cast<const float*>(ab + h->lay.r[b]);
-    GemmArgs a, c;
-    if (h->tn) {
-        char* nT = h->scratch + h->s_nT;
-        char* hT = h->scratch + h->s_hT;
-        PPS_TRY(timed(h, PPS_K_PREP_W, 0.0, (double)T * (2.0 * d + 2.0 * f) * es + (double)Tp * (d + f) * es, [&] {
-            hipError_t e = pps::transpose(dt, 1, xb, nullptr, rb, gamma, T, d, d, nT, Tp, 0, 0, h->stream);
-            if (e == hipSuccess)
-                e = pps::transpose(dt, 2, ab + h->lay.g[b], ab + h->lay.u[b], nullptr, nullptr, T, f, f, hT, Tp, 0, 0, h->stream);
-            return e;
-        }));
-        a.seg[0].A = hT; a.seg[0].lda = Tp; a.seg[0].B = dy; a.seg[0].ldb = Tp;
-        a.b_kcontig = true; a.a_kcontig = true;
-        c.seg[0].A = nT; c.seg[0].lda = Tp; c.seg[0].B = dgu; c.seg[0].ldb = Tp;
-        c.b_kcontig = true; c.a_kcontig = true;
-    } else {
-        char* sn = h->scratch + h->s_n;
-        char* sh = h->scratch + h->s_h;
+    char* sn = h->scratch + h->s_n;
+    char* sh = h->scratch + h->s_h;
+    if (!have_nh) {
+        const char* xb = act_x(h, slot, b);
+        const float* rb = reinterpret_cast<const float*>(ab + h->lay.r[b]);
         PPS_TRY(timed(h, PPS_K_PREP_W, 0.0, (double)T * (2.0 * d + 3.0 * f) * es + T * 4.0 + d * 4.0, [&] {
             return pps::prep_w(dt, xb, rb, gamma, ab + h->lay.g[b], ab + h->lay.u[b], T, d, f, sn, sh, h->stream);
         }));
-        a.seg[0].A = sh; a.seg[0].lda = f; a.seg[0].B = dy; a.seg[0].ldb = d;
-        a.a_kcontig = false; a.b_kcontig = false;
-        c.seg[0].A = sn; c.seg[0].lda = d; c.seg[0].B = dgu; c.seg[0].ldb = 2 * f;
-        c.a_kcontig = false; c.b_kcontig = false;
     }
-    a.M = f; a.N = d; a.nseg = 1; a.seg[0].K = T;
+    GemmArgs a, c;
+    a.M = f; a.N = d; a.nseg = 1;
+    a.seg[0].A = sh; a.seg[0].lda = f; a.seg[0].B = dy; a.seg[0].ldb = d; a.seg[0].K = T;
+    a.a_kcontig = false; a.b_kcontig = false;
     a.epi = pps::EPI_ACC_F32;
     a.e.out0 = dWd; a.e.ld0 = d; a.e.nsplit = d;
     PPS_TRY(timed(h, PPS_K_WGRAD_DOWN, gemm_flops(f, d, T), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
-    c.M = d; c.N = 2 * f; c.nseg = 1; c.seg[0].K = T;
+    c.M = d; c.N = 2 * f; c.nseg = 1;
+    c.seg[0].A = sn; c.seg[0].lda = d; c.seg[0].B = dgu; c.seg[0].ldb = 2 * f; c.seg[0].K = T;
+    c.a_kcontig = false; c.b_kcontig = false;
     c.epi = pps::EPI_ACC_F32;
     c.e.out0 = dWg; c.e.ld0 = f; c.e.out1 = dWu; c.e.ld1 = f; c.e.nsplit = f;
     PPS_TRY(timed(h, PPS_K_WGRAD_GATEUP, gemm_flops(d, 2.0 * f, T), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
@@ -403,7 +374,7 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
         if (rc != PPS_OK) return rc;
     }
     char* ab = acts(h, slot);
-    if (h->split && !h->tn) {
+    if (h->split) {
         // Keep this micro-batch's output gradient for the deferred W.
         char* dst = sb + h->lay.dy[D.L - 1];
         PPS_TRY(timed(h, PPS_K_COPY, 0.0, 2.0 * T * d * es, [&] { return pps::copy_bytes(dst, dy_in, T * d * es, h->stream); }));
@@ -416,7 +387,7 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
         const void* dy;
         void* dx;
         char* dgu;
-        if (h->split && !h->tn) {
+        if (h->split) {
             dy = sb + h->lay.dy[b];
             dx = b == 0 ? dx_out : static_cast<void*>(sb + h->lay.dy[b - 1]);
             dgu = sb + h->lay.dgu[b];
@@ -425,7 +396,10 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
             dx = b == 0 ? dx_out : static_cast<void*>(dxbuf[b & 1]);
             dgu = h->scratch + h->s_dgu;
         }
-        // dh = dy Wd^T, then dg, du from the stashed g, u.
+        // dh = dy Wd^T, then dg, du from the stashed g, u (and, for this
+        // block's weight gradient right after, h = silu(g) u).
+        char* sn = h->split ? nullptr : h->scratch + h->s_n;
+        char* sh = h->split ? nullptr : h->scratch + h->s_h;
         GemmArgs a;
         a.M = T; a.N = f; a.nseg = 1;
         a.seg[0].A = dy; a.seg[0].lda = d; a.seg[0].K = d;
@@ -433,7 +407,7 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
         a.a_kcontig = true; a.b_kcontig = true;
         a.epi = pps::EPI_SWIGLU_BWD;
         a.e.in0 = ab + h->lay.g[b]; a.e.in1 = ab + h->lay.u[b]; a.e.ldi0 = f;
-        a.e.out0 = dgu; a.e.ld0 = 2 * f; a.e.nsplit = f;
+        a.e.out0 = dgu; a.e.ld0 = 2 * f; a.e.nsplit = f; a.e.out2 = sh;
         PPS_TRY(timed(h, PPS_K_DH, gemm_flops(T, f, d), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
         // dn = dg Wg^T + du Wu^T (one accumulator, K = 2 ffn).
         GemmArgs c;
@@ -444,31 +418,21 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
         c.epi = pps::EPI_STORE_F32;
         c.e.out0 = dn; c.e.ld0 = d;
         PPS_TRY(timed(h, PPS_K_DN, gemm_flops(T, d, 2.0 * f), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
-        // bf16: the W GEMMs read dy and dg|du transposed; keep them (split: in
-        // the stash until W) before dy's buffer is reused.
-        const void* wdy = dy;
-        const void* wdgu = dgu;
-        if (h->tn) {
-            void* dyT = h->split ? static_cast<void*>(sb + h->lay.dy[b]) : static_cast<void*>(h->scratch + h->s_dyT);
-            void* dguT = h->split ? static_cast<void*>(sb + h->lay.dgu[b]) : static_cast<void*>(h->scratch + h->s_dguT);
-            int rc = swiglu_stage_w_operands(h, dy, dgu, dyT, dguT);
-            if (rc != PPS_OK) return rc;
-            wdy = dyT;
-            wdgu = dguT;
-        }
-        // RMSNorm backward + residual, dgamma partials, then their fixed-order sum.
+        // RMSNorm backward + residual, dgamma partials, then their fixed-order
+        // sum; without the split, also n for this block's weight gradient.
         int nrows = 0;
         PPS_TRY(timed(h, PPS_K_RMSNORM_BWD, 0.0,
-                      (double)T * d * 4 + 3.0 * T * d * es + T * 4.0 + d * 4.0 + (double)pps::rmsnorm_bwd_partial_rows(T) * d * 4, [&] {
+                      (double)T * d * 4 + (sn ? 4.0 : 3.0) * T * d * es + T * 4.0 + d * 4.0 +
+                          (double)pps::rmsnorm_bwd_partial_rows(T) * d * 4, [&] {
                           return pps::rmsnorm_bwd(dt, dn, act_x(h, slot, b), reinterpret_cast<const float*>(ab + h->lay.r[b]),
-                                                  gamma, dy, T, d, dx, part, &nrows, h->stream);
+                                                  gamma, dy, T, d, dx, part, &nrows, sn, h->stream);
                       }));
         const int prow = pps::rmsnorm_bwd_partial_rows(T);
         PPS_TRY(timed(h, PPS_K_DGAMMA, 0.0, (double)prow * d * 4 + 8.0 * d, [&] {
             return pps::column_reduce_acc(part, T > 0 ? prow : 0, d, dgam, h->stream);
         }));
         if (!h->split) {
-            int rc = swiglu_weight(h, slot, chunk, b, wdy, wdgu);
+            int rc = swiglu_weight(h, slot, chunk, b, dy, dgu, true);
             if (rc != PPS_OK) return rc;
         }
     }
@@ -478,7 +442,7 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
 int swiglu_backward_weight(pps_stage* h, int slot, int chunk) {
     char* sb = slot_base(h, slot);
     for (int b = h->d.L - 1; b >= 0; --b) {
-        int rc = swiglu_weight(h, slot, chunk, b, sb + h->lay.dy[b], sb + h->lay.dgu[b]);
+        int rc = swiglu_weight(h, slot, chunk, b, sb + h->lay.dy[b], sb + h->lay.dgu[b], false);
         if (rc != PPS_OK) return rc;
     }
     return PPS_OK;
@@ -603,9 +567,8 @@ extern "C" int pps_stage_create(const pps_stage_desc* desc, pps_stage** out) {
     h->slot_used.assign(h->S, 0);
 
     h->tn = h->swiglu && desc->dtype == PPS_DTYPE_BF16;
-    h->Tp = (desc->T + 7) / 8 * 8;
-    h->lay = make_layout(*desc, h->swiglu, h->split, h->es, h->tn, h->Tp);
-    const size_t T = (size_t)desc->T, dm = (size_t)desc->d, f = (size_t)desc->ffn, Tp = (size_t)h->Tp;
+    h->lay = make_layout(*desc, h->swiglu, h->split, h->es);
+    const size_t T = (size_t)desc->T, dm = (size_t)desc->d, f = (size_t)desc->ffn;
     size_t off = 0;
     auto take = [&](size_t& o, size_t bytes) { o = off; off += align256(bytes); };
     if (h->ac) {
@@ -617,14 +580,10 @@ extern "C" int pps_stage_create(const pps_stage_desc* desc, pps_stage** out) {
     if (h->swiglu) {
         take(h->s_n, T * dm * h->es);
         take(h->s_h, T * f * h->es);
-        take(h->s_dgu, (h->split && !h->tn) ? 256 : T * 2 * f * h->es);
+        take(h->s_dgu, h->split ? 256 : T * 2 * f * h->es);
         take(h->s_dn, T * dm * 4);
         take(h->s_part, (size_t)pps::rmsnorm_bwd_partial_rows((int64_t)T) * dm * 4);
         if (h->tn) {
-            take(h->s_nT, dm * Tp * 2);
-            take(h->s_hT, f * Tp * 2);
-            take(h->s_dguT, h->split ? 256 : 2 * f * Tp * 2);
-            take(h->s_dyT, h->split ? 256 : dm * Tp * 2);
             size_t w = 0;
             for (int i = 0; i < desc->v * desc->L; ++i) {
                 h->wgu_off.push_back(w);
