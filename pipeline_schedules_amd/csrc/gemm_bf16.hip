@@ -7,33 +7,39 @@
 // K-contiguous copies of the weights); the weight-gradient GEMMs dW = X^T Y
 // reduce over tokens and read the activations and gradients as they are
 // stored, [T, features], in the MN mode, which needs no transposed copies.
+// Both kernels tile 256 x 256 x 64, take both operands straight from memory
+// into LDS (direct-to-LDS buffer loads, no register staging) and read zeros
+// outside an operand's extent, which pads ragged M, N and K tails.
 //
-// Tiling: macro-tile 256 x 256 x 64, 512 threads = 8 wavefronts in a 2 x 4
-// grid, 128 x 64 per wavefront = 4 x 2 tiles of v_mfma_f32_32x32x16_bf16
-// (128 fp32 accumulators per lane, two wavefronts per SIMD).
+// TN kernel: 256 threads = 4 wavefronts in a 2 x 2 grid, one per SIMD,
+// 128 x 128 per wavefront = 8 x 8 tiles of v_mfma_f32_16x16x32_bf16 (256
+// fp32 accumulators per lane, in AGPRs).  LDS holds a ring of five 32 KB
+// operand-tile slots, A of K tile t in slot 2t mod 5 and B in slot 2t+1 mod 5.
+// Within a K step on tile t every fragment of tile t is read into registers
+// by mid-step (the second K half under the first half's MFMAs); a mid-step
+// barrier then frees tile t's slots.  Tile t+2's A is requested during the
+// first half (into B(t-1)'s slot), its B during the second half (into A(t)'s
+// slot), one request per few MFMAs, so each tile has at least a full step to
+// arrive.  The step ends with vmcnt(16) (everything but tile t+2) and a
+// barrier, after which tile t+1's first-half fragments are read under the
+// last 16 MFMAs, in the order a0 b0 a1 b1 ... that the MFMAs consume them
+// (growing squares over the 8 x 8 tiles).  LDS rows are 128 bytes; 16-byte
+// chunk c of row r sits at position c ^ ((r >> 1) & 7), which keeps the
+// direct-to-LDS writes and the fragment reads free of bank conflicts.
 //
-// Data path: both operands go straight from memory to LDS (direct-to-LDS
-// buffer loads, no register staging).  A tiles are requested two K steps
-// before they are multiplied, into three 32 KB slots; B tiles one step ahead,
-// into two 32 KB slots (160 KB of LDS in all); the requests are spread over
-// the MFMAs of the step.  One barrier per K step; MFMA operands are read with
-// ds_read_b128.  The stage's GEMMs run at the chip's power limit, so what the
-// loop saves is energy: no register round trip and no LDS store instructions
-// for the operands.  In LDS, 16-byte chunk c
-// of row r sits at position c ^ ((r >> 1) & 7), which keeps the 16 lanes of
-// every ds_read_b128 phase on distinct banks (64 banks, two 128-byte rows
-// per bank period).  Buffer loads return zero outside the operand's extent,
-// which pads ragged M, N and K tails without branches.
+// Why this shape: the stage GEMMs run at the chip's power limit, so what
+// counts is work per cycle and energy per FLOP.  A lone wavefront per SIMD
+// reading 128 x 128 per K step needs a third fewer LDS reads than two
+// wavefronts of 128 x 64, and the 16x16x32 MFMA moves half the accumulator
+// data of the 32x32x16 one per FLOP.  A lone wavefront has no partner to
+// cover its non-MFMA instructions, so the K loop is unrolled over the five
+// ring phases: every slot offset is an immediate and the load masks for the
+// K tail live in a separate tail loop, which leaves one M0 write per load and
+// the LDS reads between the MFMAs.
 //
-// MN mode: an operand tile is 64 k-rows of 256 M (or N) values, 512 bytes
-// each; 16-byte chunk c of k-row k sits at position c ^ (4 * (k & 3)).  Each
-// load instruction moves two k-rows.  MFMA fragments, which hold 8
-// consecutive k per lane, come from two ds_read_b64_tr_b16 each (the LDS
-// transposes 4 x 4 blocks of 16-bit values across lanes on the way out); the
-// swizzle keeps both the loads' writes and these reads free of bank
-// conflicts.  Twice the LDS read instructions of the TN mode for the same
-// bytes; the per-lane read addresses are fixed, with the K sub-step and the
-// slot in the immediate offset and one scalar base.
+// MN kernel (weight gradients): 8 wavefronts of 128 x 64 with
+// v_mfma_f32_32x32x16_bf16 and transposing LDS reads (ds_read_b64_tr_b16);
+// it is described where it is defined.
 //
 // Workgroup -> tile mapping: the dispatcher places workgroup i on XCD i % 8;
 // ids are remapped so each XCD gets a contiguous run of logical tiles, and
@@ -49,16 +55,19 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHREADS = 512;
-constexpr int ROWB = BK * 2;             // 128 bytes per LDS row
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int NTHREADS = 256;            // TN kernel: 4 wavefronts
+constexpr int MN_THREADS = 512;          // M/N-contiguous kernel: 8 wavefronts
+constexpr int NQ = 8;                    // TN: 1 KB load pieces per wavefront per operand tile
+constexpr int ROWB = BK * 2;             // TN: 128 bytes per LDS row
 constexpr int OPB = 256 * ROWB;          // 32 KB per operand tile
-constexpr int ASLOTS = 3, BSLOTS = 2;    // LDS slots of A (direct loads) and B (from registers)
-constexpr int BBASE = ASLOTS * OPB;
-constexpr int LDS_BYTES = (ASLOTS + BSLOTS) * OPB;   // 160 KB
+constexpr int NSLOT = 5;                 // operand-tile slots
+constexpr int LDS_BYTES = NSLOT * OPB;   // 160 KB
 constexpr int GROUP_M = 8;
 constexpr uint32_t OOB = 0x80000000u;    // an offset past every operand extent
 
@@ -95,11 +104,11 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
 }
 
 // ---- epilogue ---------------------------------------------------------------
-// A 32x32 MFMA accumulator gives lane l column l%32 and, for element group q,
-// rows q*8 + (l/32)*4 + 0..3.  A 4x4 transpose inside each lane quad (DPP quad
-// permutes) turns that into row q*8 + (l/32)*4 + l%4 and columns 4*(l%32/4) +
-// 0..3, so every global access of the epilogue is an 8-byte (bf16) or 16-byte
-// (fp32) vector and one wavefront access covers 8 rows x 32 columns.
+// A 16x16 MFMA accumulator gives lane l column l%16 and rows 4*(l/16) + 0..3;
+// a 32x32 one column l%32 and, for element group q, rows q*8 + 4*(l/32) +
+// 0..3.  A 4x4 transpose inside each lane quad (DPP quad permutes) gives each
+// lane one row and four consecutive columns, so every global access of the
+// epilogue is an 8-byte (bf16) or 16-byte (fp32) vector.
 
 template <int CTRL>
 __device__ __forceinline__ float quad_xor(float x) {
@@ -230,30 +239,345 @@ __device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t lds, uint32_t voff
                  :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
 }
 
-template <int EPI, bool MN>
+// MFMA x (0..63) of a K half in growing squares over the 8 x 8 tiles, so the
+// x-th MFMA needs only fragments a[0..m], b[0..m] (read as a0 b0 a1 b1 ...).
+constexpr int ord_i(int x) {
+    int m = 0;
+    while ((m + 1) * (m + 1) <= x) ++m;
+    const int r = x - m * m;
+    return r <= m ? m : r - m - 1;
+}
+constexpr int ord_j(int x) {
+    int m = 0;
+    while ((m + 1) * (m + 1) <= x) ++m;
+    const int r = x - m * m;
+    return r <= m ? r : m;
+}
+
+// ---- K-contiguous kernel ----------------------------------------------------
+template <int EPI>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t n0 = (int64_t)tn * (p.swiglu ? BN / 2 : BN);   // first output column
+    const int64_t nb0 = (int64_t)tn * BN;                         // first B row
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+
+    // Loader: each wavefront moves NQ pieces of 1 KB per operand tile; piece q
+    // holds LDS rows (wave*NQ+q)*8 .. +7, lane l row + l/8 at position l&7,
+    // i.e. logical chunk lcq[q] = (l&7) ^ ((row>>1)&7).  Per-lane byte
+    // offsets stay fixed within a K segment; the K step rides in soffset.
+    int lcq[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) lcq[q] = (lane & 7) ^ ((((wave * NQ + q) * 8 + (lane >> 3)) >> 1) & 7);
+    uint32_t aoff[NQ], boff[NQ];
+    rsrc_t ar, br;
+    int64_t K = 0;
+    int nk = 0;
+    auto set_seg = [&](int s) __attribute__((always_inline)) {
+        const Seg g = s == 0 ? p.seg[0] : p.seg[1];   // no dynamic index into the arguments
+        ar = make_rsrc(g.A, g.a_bytes);
+        br = make_rsrc(g.B, g.b_bytes);
+        K = g.K;
+        nk = (int)((K + BK - 1) / BK);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int row = (wave * NQ + q) * 8 + (lane >> 3);
+            const int64_t ra = m0 + row, rb = nb0 + row;
+            aoff[q] = ra < p.M ? (uint32_t)(ra * g.lda * 2 + lcq[q] * 16) : OOB;
+            boff[q] = rb < p.NB ? (uint32_t)(rb * g.ldb * 2 + lcq[q] * 16) : OOB;
+        }
+    };
+    // Piece q of K tile kt holds K chunk lcq[q]: in range if it starts before K.
+    auto kin = [&](int kt, int q) __attribute__((always_inline)) {
+        return (int64_t)lcq[q] * 8 < K - (int64_t)kt * BK;
+    };
+    // Load piece q of operand tile kt into `slot` (masked: chunks past K read
+    // zeros through the out-of-range offset).
+    auto load = [&](auto isa_c, int slot, int kt, int q, bool masked) __attribute__((always_inline)) {
+        constexpr bool ISA = decltype(isa_c)::value;
+        const uint32_t o = (!masked || kin(kt, q)) ? (ISA ? aoff[q] : boff[q]) : OOB;
+        const int lo = slot * OPB + (wave_s * NQ + q) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ISA ? ar : br, (LDS_AS void*)(smem + lo), 16, o, (uint32_t)kt * (BK * 2),
+                                                 0, 0);
+    };
+    using TA = std::true_type;
+    using TB = std::false_type;
+
+    // Fragments: A fragment i of K half s is rows wm*128 + i*16 + l%16,
+    // logical chunk 4s + l/16 at position chunk ^ ((row>>1)&7) = chunk ^ fsw;
+    // the per-lane base is fixed, the slot and i*16 rows are immediates.
+    const int fsw = ((lane & 15) >> 1) & 7;
+    const int pc0 = ((lane >> 4) ^ fsw) << 4, pc1 = ((4 + (lane >> 4)) ^ fsw) << 4;
+    const char* fA = smem + (wm * 128 + (lane & 15)) * ROWB;
+    const char* fB = smem + (wn * 128 + (lane & 15)) * ROWB;
+    bf16x8 fa[2][8], fb[2][8];
+    // fragment x (0..15) of K half s of the tile in slots (sa, sb): a0 b0 a1 b1 ...
+    auto fragx = [&](int sa, int sb, int s, int x, bf16x8 (&a)[8], bf16x8 (&b)[8]) __attribute__((always_inline)) {
+        const int y = x >> 1, pc = s ? pc1 : pc0;
+        if ((x & 1) == 0) a[y] = *reinterpret_cast<const bf16x8*>(fA + sa * OPB + y * 16 * ROWB + pc);
+        else b[y] = *reinterpret_cast<const bf16x8*>(fB + sb * OPB + y * 16 * ROWB + pc);
+    };
+
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    auto mm = [&](const bf16x8 (&a)[8], const bf16x8 (&b)[8], int lo, int hi) __attribute__((always_inline)) {
+#pragma unroll
+        for (int x = 0; x < 64; ++x)
+            if (x >= lo && x < hi) {
+                const int i = ord_i(x), j = ord_j(x);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            }
+    };
+
+    // One K step on tile kt.  PH = kt % 5 when known at compile time (slot
+    // offsets become immediates); MASK: tile kt+2 may reach past K.
+    auto step = [&](auto ph_c, auto mask_c, int kt) __attribute__((always_inline)) {
+        constexpr int PH = decltype(ph_c)::value;
+        constexpr bool MASK = decltype(mask_c)::value;
+        const int ph = PH >= 0 ? PH : kt % 5;
+        const int sA = (2 * ph) % 5, sB = (2 * ph + 1) % 5;          // tile kt
+        const int sA1 = (2 * ph + 2) % 5, sB1 = (2 * ph + 3) % 5;    // tile kt+1
+        const int sA2 = (2 * ph + 4) % 5, sB2 = (2 * ph + 5) % 5;    // tile kt+2
+        // first half: MFMAs on half 0; tile kt+2's A; half 1's fragments
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            mm(fa[0], fb[0], 8 * r, 8 * r + 8);
+            __builtin_amdgcn_sched_barrier(0);
+            load(TA{}, sA2, kt + 2, r, MASK);
+            if (r < 4) {
+#pragma unroll
+                for (int y = 0; y < 4; ++y) fragx(sA, sB, 1, 4 * r + y, fa[1], fb[1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // this wavefront's reads of tile kt are done; after the barrier no
+        // wavefront reads its slots
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt open
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // second half: MFMAs on half 1; tile kt+2's B into A(kt)'s slot
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            load(TB{}, sB2, kt + 2, r, MASK);
+            __builtin_amdgcn_sched_barrier(0);
+            mm(fa[1], fb[1], 6 * r, 6 * r + 6);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // vmcnt(16): all but tile kt+2's requests, i.e. tile kt+1, have landed
+        wait_vm_lgkm0<2 * NQ>();
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            fragx(sA1, sB1, 0, r, fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            mm(fa[1], fb[1], 48 + r, 49 + r);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
+    using P4 = std::integral_constant<int, 4>;
+    using PR = std::integral_constant<int, -1>;
+
+    for (int s = 0; s < p.nseg; ++s) {
+        set_seg(s);
+        if (nk == 0) continue;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) { load(TA{}, 0, 0, q, true); load(TB{}, 1, 0, q, true); }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) { load(TA{}, 2, 1, q, true); load(TB{}, 3, 1, q, true); }
+        wait_vm_lgkm0<2 * NQ>();   // tile 0 in LDS
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            fragx(0, 1, 0, x, fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // unmasked while tile kt+2 lies wholly inside K
+        const int nfull = (int)(K / BK);
+        int kt = 0;
+        for (; kt + 7 <= nfull; kt += 5) {
+            step(P0{}, std::false_type{}, kt);
+            step(P1{}, std::false_type{}, kt + 1);
+            step(P2{}, std::false_type{}, kt + 2);
+            step(P3{}, std::false_type{}, kt + 3);
+            step(P4{}, std::false_type{}, kt + 4);
+        }
+        for (; kt < nk; ++kt) step(PR{}, std::true_type{}, kt);
+        // the last steps requested all-zero tiles past K: let them land
+        // before another segment reuses the slots (and before the epilogue)
+        wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+    }
+
+    // Epilogue on quad-transposed accumulators: this lane owns tile row
+    // lr + 16i and tile columns lc + 16j .. +3 (SwiGLU: hidden columns lc +
+    // 16jj from the gate tile {0,1,4,5}[jj] and the up tile two further).
+    const int jq = lane & 3;
+    const int lr = wm * 128 + 4 * (lane >> 4) + jq;
+    const int lc = (p.swiglu ? wn * 64 : wn * 128) + 4 * ((lane >> 2) & 3);
+    const EpiArgs e = p.e;
+    const int64_t pM = p.M, pN = p.N;
+    constexpr int ESO = (EPI == EPI_STORE_F32 || EPI == EPI_ACC_F32) ? 4 : 2;   // output element bytes
+    constexpr bool HAS_IN = EPI == EPI_RESID || EPI == EPI_SWIGLU_BWD || EPI == EPI_ACC_F32;
+    constexpr int PD = 1;   // row groups loaded ahead
+    EpiIn<EPI> in[PD + 1][8];
+
+    // Whole tile inside M x N (and, for the split fp32 accumulate, on one side
+    // of nsplit): every operand is a uniform per-tile base plus this lane's
+    // fixed 32-bit offset plus a uniform per-(i, j) offset, so the accesses
+    // need no bounds checks and no per-element 64-bit index arithmetic.
+    bool fast = m0 + BM <= pM && n0 + (p.swiglu ? BN / 2 : BN) <= pN;
+    char* ob = nullptr;            // output tile base
+    int64_t old = e.ld0;           // its leading dimension (elements)
+    if constexpr (EPI == EPI_ACC_F32) {
+        if (n0 + BN <= e.nsplit) {
+            ob = static_cast<char*>(e.out0) + (m0 * e.ld0 + n0) * 4;
+        } else if (n0 >= e.nsplit) {
+            ob = static_cast<char*>(e.out1) + (m0 * e.ld1 + (n0 - e.nsplit)) * 4;
+            old = e.ld1;
+        } else {
+            fast = false;
+        }
+    } else {
+        ob = static_cast<char*>(e.out0) + (m0 * e.ld0 + n0) * ESO;
+    }
+    const uint32_t lo = (uint32_t)(((int64_t)lr * old + lc) * ESO);
+    const uint32_t li = (uint32_t)(((int64_t)lr * e.ldi0 + lc) * 2);
+    auto fptr = [&](int i, int j) __attribute__((always_inline)) -> EpiPtr {
+        const int64_t uo = ((int64_t)(i * 16) * old + j * 16) * ESO;
+        EpiPtr a{};
+        char* o = ob + uo + lo;
+        a.o0 = o;
+        if constexpr (EPI == EPI_SWIGLU) {
+            a.o1 = static_cast<char*>(e.out1) + (m0 * e.ld0 + n0) * 2 + uo + lo;
+            a.o2 = static_cast<char*>(e.out2) + (m0 * e.ld0 + n0) * 2 + uo + lo;
+        } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+            a.o1 = o + e.nsplit * 2;
+            const int64_t ui = ((int64_t)(i * 16) * e.ldi0 + j * 16 + m0 * e.ldi0 + n0) * 2;
+            a.i0 = static_cast<const char*>(e.in0) + ui + li;
+            a.i1 = static_cast<const char*>(e.in1) + ui + li;
+            a.o2 = e.out2 ? static_cast<char*>(e.out2) + ui + li : nullptr;
+        } else if constexpr (EPI == EPI_RESID) {
+            const int64_t ui = ((int64_t)(i * 16) * e.ldi0 + j * 16 + m0 * e.ldi0 + n0) * 2;
+            a.i0 = static_cast<const char*>(e.in0) + ui + li;
+        } else if constexpr (EPI == EPI_ACC_F32) {
+            a.i0 = o;
+        }
+        return a;
+    };
+    auto sptr = [&](int64_t row, int64_t col) __attribute__((always_inline)) -> EpiPtr {
+        EpiPtr a{};
+        if constexpr (EPI == EPI_ACC_F32) {
+            float* c = acc_ptr(e, row, col);
+            a.o0 = reinterpret_cast<char*>(c);
+            a.i0 = reinterpret_cast<const char*>(c);
+        } else {
+            a.o0 = static_cast<char*>(e.out0) + (row * e.ld0 + col) * ESO;
+            if constexpr (EPI == EPI_SWIGLU) {
+                a.o1 = static_cast<char*>(e.out1) + (row * e.ld0 + col) * 2;
+                a.o2 = static_cast<char*>(e.out2) + (row * e.ld0 + col) * 2;
+            } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+                a.o1 = a.o0 + e.nsplit * 2;
+                a.i0 = static_cast<const char*>(e.in0) + (row * e.ldi0 + col) * 2;
+                a.i1 = static_cast<const char*>(e.in1) + (row * e.ldi0 + col) * 2;
+                a.o2 = e.out2 ? static_cast<char*>(e.out2) + (row * e.ldi0 + col) * 2 : nullptr;
+            } else if constexpr (EPI == EPI_RESID) {
+                a.i0 = static_cast<const char*>(e.in0) + (row * e.ldi0 + col) * 2;
+            }
+        }
+        return a;
+    };
+
+    constexpr int NJ = EPI == EPI_SWIGLU ? 4 : 8;   // column groups per row group
+    auto run = [&](auto fast_c) __attribute__((always_inline)) {
+        constexpr bool FAST = decltype(fast_c)::value;
+        auto ptr = [&](int i, int j) __attribute__((always_inline)) -> EpiPtr {
+            if constexpr (FAST) return fptr(i, j);
+            else return sptr(m0 + lr + i * 16, n0 + lc + j * 16);
+        };
+        auto ok = [&](int i, int j) __attribute__((always_inline)) -> bool {
+            if constexpr (FAST) return true;
+            else return m0 + lr + i * 16 < pM && n0 + lc + j * 16 < pN;
+        };
+        auto prefetch = [&](int i, EpiIn<EPI> (&dst)[8]) __attribute__((always_inline)) {
+            if constexpr (HAS_IN) {
+#pragma clang loop unroll(full)
+                for (int j = 0; j < NJ; ++j)
+                    if (ok(i, j)) epi_load<EPI>(ptr(i, j), dst[j]);
+            }
+        };
+        auto tr = [&](int i, int j, float (&w)[4]) __attribute__((always_inline)) {
+            const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+            quad_transpose(v, w, (jq & 1) != 0, (jq & 2) != 0);
+        };
+#pragma clang loop unroll(full)
+        for (int i = 0; i < PD; ++i) prefetch(i, in[i]);
+#pragma clang loop unroll(full)
+        for (int i = 0; i < 8; ++i) {
+            if (i + PD < 8) prefetch(i + PD, in[(i + PD) % (PD + 1)]);
+#pragma clang loop unroll(full)
+            for (int j = 0; j < NJ; ++j) {
+                if constexpr (EPI == EPI_SWIGLU) {
+                    // B rows of a wavefront: 32 gate, 32 up, 32 gate, 32 up rows
+                    const int gj = (j >> 1) * 4 + (j & 1);
+                    float g[4], u[4];
+                    tr(i, gj, g);
+                    tr(i, gj + 2, u);
+                    if (ok(i, j)) epi4_swiglu(ptr(i, j), g, u);
+                } else {
+                    float w[4];
+                    tr(i, j, w);
+                    if (ok(i, j)) epi4<EPI>(ptr(i, j), w, in[i % (PD + 1)][j]);
+                }
+            }
+        }
+    };
+    if (fast) run(std::true_type{});
+    else run(std::false_type{});
+}
+
+// ---- M/N-contiguous kernel (weight gradients) -------------------------------
+// 512 threads = 8 wavefronts in a 2 x 4 grid, 128 x 64 per wavefront = 4 x 2
+// tiles of v_mfma_f32_32x32x16_bf16.  A tiles are requested two K steps
+// ahead into three 32 KB slots, B tiles one step ahead into two; one barrier
+// per K step.  An operand tile is 64 k-rows x 256 values, 512 B per k-row,
+// 16-byte chunk c of k-row k at position c ^ 4 (k & 3); each load moves two
+// k-rows, and a 32x32x16 fragment (lane l: column l % 32, k = 8 (l / 32) ..
+// +7) comes from two ds_read_b64_tr_b16.  The transposing read's lane layout,
+// probed on the GPU: within each group of 16 lanes, lane j receives element
+// (j & 3) of the 8-byte blocks addressed by lanes 4e + (j >> 2), e = 0..3.
+template <int EPI>
+__global__ __launch_bounds__(MN_THREADS, 1) void gemm_mn_kernel(const Params p) {
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+    constexpr int ASLOTS = 3;              // A slots; B has two after them
+    constexpr int BBASE = ASLOTS * OPB;
 
     int tm, tn;
     tile_coords(p, tm, tn);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * (p.swiglu ? BN / 2 : BN);   // first output column
-    const int64_t nb0 = (int64_t)tn * BN;                         // first B row
+    const int64_t n0 = (int64_t)tn * BN;   // first output column
+    const int64_t nb0 = n0;                // first B row
 
-    // Loader: per K step each wavefront moves 4 A and 4 B pieces of 1 KB; piece
-    // q holds LDS rows (wave*4+q)*8 .. +7; lane l covers row + l/8 and LDS chunk
-    // l&7, i.e. logical chunk lcq[q] = (l&7) ^ ((row>>1)&7).  The per-lane byte
-    // offsets stay fixed within a K segment; the K step rides in soffset.
-    const int lrow = lane >> 3;
+    // Loader: per K step each wavefront moves 4 A and 4 B pieces of 1 KB;
+    // piece q holds k-rows kq[q] = (wave*4+q)*2 + l/32, lane l the LDS chunk
+    // l&31 = logical chunk (l&31) ^ 4*(kq[q]&3); the K step (64 k-rows) rides
+    // in soffset.
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    int lcq[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lcq[q] = (lane & 7) ^ (((wave * 4 + q) * 4 + (lane >> 4)) & 7);
-    // MN mode: piece q holds k-rows kq[q] = (wave*4+q)*2 + l/32, lane l the
-    // LDS chunk l&31 = logical chunk (l&31) ^ 4*(kq[q]&3); the K step (64
-    // k-rows) rides in soffset.
     int kq[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) kq[q] = (wave * 4 + q) * 2 + (lane >> 5);
@@ -262,62 +586,39 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         return col < ncols ? (uint32_t)((kq[q] * ld + col) * 2) : OOB;
     };
     uint32_t aoff[4], boff[4];
-    uint32_t astep = BK * 2, bstep = BK * 2;   // bytes per K step
+    uint32_t astep = 0, bstep = 0;   // bytes per K step
     rsrc_t ar, br;
     int64_t K = 0;
+    int nk = 0;
     auto set_seg = [&](int s) {
-        const Seg& g = p.seg[s];
+        const Seg g = s == 0 ? p.seg[0] : p.seg[1];
         ar = make_rsrc(g.A, g.a_bytes);
         br = make_rsrc(g.B, g.b_bytes);
         K = g.K;
-        if constexpr (MN) {
-            astep = (uint32_t)(BK * g.lda * 2);
-            bstep = (uint32_t)(BK * g.ldb * 2);
-        }
+        nk = (int)((K + BK - 1) / BK);
+        astep = (uint32_t)(BK * g.lda * 2);
+        bstep = (uint32_t)(BK * g.ldb * 2);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            if constexpr (MN) {
-                aoff[q] = mn_off(q, m0, p.M, g.lda);
-                boff[q] = mn_off(q, nb0, p.NB, g.ldb);
-            } else {
-                const int row = (wave * 4 + q) * 8 + lrow;
-                const int64_t ra = m0 + row, rb = nb0 + row;
-                aoff[q] = ra < p.M ? (uint32_t)(ra * g.lda * 2 + lcq[q] * 16) : OOB;
-                boff[q] = rb < p.NB ? (uint32_t)(rb * g.ldb * 2 + lcq[q] * 16) : OOB;
-            }
+            aoff[q] = mn_off(q, m0, p.M, g.lda);
+            boff[q] = mn_off(q, nb0, p.NB, g.ldb);
         }
     };
-    // Piece q of K tile kt (past the segment's K: zeros).  Branch-free, so the
-    // compiler's wait counts for the B registers stay exact across the loop.
-    auto chunks_left = [&](int kt) {
-        const int64_t rem = K - (int64_t)kt * BK;
-        return rem <= 0 ? 0 : rem >= BK ? BK / 8 : (int)rem / 8;   // valid 16-byte chunks per row
-    };
-    // In K range: TN pieces hold 16-byte K chunks, MN pieces whole k-rows.
-    auto kin = [&](int kt, int q) {
-        if constexpr (MN) return kq[q] < (int)(K - (int64_t)kt * BK);
-        else return lcq[q] < chunks_left(kt);
-    };
+    // k-rows past the segment's K read zeros; so do tiles past K, with
+    // soffset 0 so that OOB + soffset cannot wrap into the extent
+    auto kin = [&](int kt, int q) { return kq[q] < (int)(K - (int64_t)kt * BK); };
     const uint32_t lds0 = (uint32_t)(size_t)(LDS_AS char*)smem;
     auto issueA = [&](int kt, int q) {
         const int so = (kt % ASLOTS) * OPB + (wave_s * 4 + q) * 1024;
         const uint32_t ao = kin(kt, q) ? aoff[q] : OOB;
-        if constexpr (MN)
-            lds_load16(ar, lds0 + so, ao, (uint32_t)kt * astep);
-        else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (LDS_AS void*)(smem + so), 16, ao, (uint32_t)kt * astep, 0, 0);
+        lds_load16(ar, lds0 + so, ao, kt < nk ? (uint32_t)kt * astep : 0u);
     };
     auto issueB = [&](int kt, int q) {
         const int so = BBASE + (kt & 1) * OPB + (wave_s * 4 + q) * 1024;
         const uint32_t bo = kin(kt, q) ? boff[q] : OOB;
-        if constexpr (MN)
-            lds_load16(br, lds0 + so, bo, (uint32_t)kt * bstep);
-        else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (LDS_AS void*)(smem + so), 16, bo, (uint32_t)kt * bstep, 0, 0);
+        lds_load16(br, lds0 + so, bo, kt < nk ? (uint32_t)kt * bstep : 0u);
     };
 
-    // MFMA operand fragment: row r, logical chunk ch at r*128 + (ch ^ ((r>>1)&7))*16.
-    const int fsw = ((lane & 31) >> 1) & 7;
     // MN fragment of the 32 columns at cb, k = 16*kk .. +15: in 16-lane group
     // g = l/16, lane s = l%16 addresses k-row 16*kk + 8*(g>>1) + s/4 (+4 for
     // the second read) at columns cb + 16*(g&1) + 4*(s&3) .. +3, and lane j of
@@ -343,25 +644,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         return __builtin_bit_cast(bf16x8, v);
     };
     auto frags = [&](int kt, int kk, bf16x8 (&a)[4], bf16x8 (&b)[2]) {
-        if constexpr (MN) {
-            // slot bases as scalars, so the per-read offsets stay immediates
-            const uint32_t ua = __builtin_amdgcn_readfirstlane(lds0 + (kt % ASLOTS) * OPB);
-            const uint32_t ub = __builtin_amdgcn_readfirstlane(lds0 + BBASE + (kt & 1) * OPB);
+        // slot bases as scalars, so the per-read offsets stay immediates
+        const uint32_t ua = __builtin_amdgcn_readfirstlane(lds0 + (kt % ASLOTS) * OPB);
+        const uint32_t ub = __builtin_amdgcn_readfirstlane(lds0 + BBASE + (kt & 1) * OPB);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = mn_frag(ua, mn_aoff[i], kk);
+        for (int i = 0; i < 4; ++i) a[i] = mn_frag(ua, mn_aoff[i], kk);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) b[j] = mn_frag(ub, mn_boff[j], kk);
-        } else {
-            const char* sa = smem + (kt % ASLOTS) * OPB;
-            const char* sb = smem + BBASE + (kt & 1) * OPB;
-            const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) << 4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 128 + i * 32 + (lane & 31)) * ROWB + pc);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                b[j] = *reinterpret_cast<const bf16x8*>(sb + (wn * 64 + j * 32 + (lane & 31)) * ROWB + pc);
-        }
+        for (int j = 0; j < 2; ++j) b[j] = mn_frag(ub, mn_boff[j], kk);
     };
 
     f32x16 acc[4][2];
@@ -402,7 +691,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
 
     for (int s = 0; s < p.nseg; ++s) {
         set_seg(s);
-        const int nk = (int)((K + BK - 1) / BK);
         if (nk == 0) continue;
 #pragma unroll
         for (int q = 0; q < 4; ++q) { issueA(0, q); issueB(0, q); }
@@ -421,18 +709,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     const int jq = lane & 3;
     const int cq = (lane & 31) & ~3;
     const int lr = wm * 128 + (lane >> 5) * 4 + jq;
-    const int lc = (p.swiglu ? wn * 32 : wn * 64) + cq;
-    const EpiArgs& e = p.e;
-    constexpr int ESO = (EPI == EPI_STORE_F32 || EPI == EPI_ACC_F32) ? 4 : 2;   // output element bytes
-    constexpr bool HAS_IN = EPI == EPI_RESID || EPI == EPI_SWIGLU_BWD || EPI == EPI_ACC_F32;
-    constexpr int PD = EPI == EPI_RESID ? 2 : 1;   // row groups loaded ahead (registers allow)
+    const int lc = wn * 64 + cq;
+    const EpiArgs e = p.e;
+    static_assert(EPI == EPI_STORE_F32 || EPI == EPI_ACC_F32, "fp32 epilogues only");
+    constexpr int ESO = 4;                            // output element bytes
+    constexpr bool HAS_IN = EPI == EPI_ACC_F32;
+    constexpr int PD = 1;                             // row groups loaded ahead
     EpiIn<EPI> in[PD + 1][4][2];
 
     // Whole tile inside M x N (and, for the split fp32 accumulate, on one side
     // of nsplit): every operand is a uniform per-tile base plus this lane's
     // fixed 32-bit offset plus a uniform per-(i, q, j) offset, so the accesses
     // need no bounds checks and no per-element 64-bit index arithmetic.
-    bool fast = m0 + BM <= p.M && n0 + (p.swiglu ? BN / 2 : BN) <= p.N;
+    bool fast = m0 + BM <= p.M && n0 + BN <= p.N;
     char* ob = nullptr;            // output tile base
     int64_t old = e.ld0;           // its leading dimension (elements)
     if constexpr (EPI == EPI_ACC_F32) {
@@ -448,27 +737,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         ob = static_cast<char*>(e.out0) + (m0 * e.ld0 + n0) * ESO;
     }
     const uint32_t lo = (uint32_t)(((int64_t)lr * old + lc) * ESO);
-    const uint32_t li = (uint32_t)(((int64_t)lr * e.ldi0 + lc) * 2);
     auto fptr = [&](int i, int q, int j) -> EpiPtr {
         const int64_t uo = ((int64_t)(i * 32 + q * 8) * old + j * 32) * ESO;
         EpiPtr a{};
         char* o = ob + uo + lo;
         a.o0 = o;
-        if constexpr (EPI == EPI_SWIGLU) {
-            a.o1 = static_cast<char*>(e.out1) + (m0 * e.ld0 + n0) * 2 + uo + lo;
-            a.o2 = static_cast<char*>(e.out2) + (m0 * e.ld0 + n0) * 2 + uo + lo;
-        } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-            a.o1 = o + e.nsplit * 2;
-            const int64_t ui = ((int64_t)(i * 32 + q * 8) * e.ldi0 + j * 32 + m0 * e.ldi0 + n0) * 2;
-            a.i0 = static_cast<const char*>(e.in0) + ui + li;
-            a.i1 = static_cast<const char*>(e.in1) + ui + li;
-            a.o2 = e.out2 ? static_cast<char*>(e.out2) + ui + li : nullptr;
-        } else if constexpr (EPI == EPI_RESID) {
-            const int64_t ui = ((int64_t)(i * 32 + q * 8) * e.ldi0 + j * 32 + m0 * e.ldi0 + n0) * 2;
-            a.i0 = static_cast<const char*>(e.in0) + ui + li;
-        } else if constexpr (EPI == EPI_ACC_F32) {
-            a.i0 = o;
-        }
+        if constexpr (EPI == EPI_ACC_F32) a.i0 = o;
         return a;
     };
     auto sptr = [&](int64_t row, int64_t col) -> EpiPtr {
@@ -479,17 +753,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
             a.i0 = reinterpret_cast<const char*>(c);
         } else {
             a.o0 = static_cast<char*>(e.out0) + (row * e.ld0 + col) * ESO;
-            if constexpr (EPI == EPI_SWIGLU) {
-                a.o1 = static_cast<char*>(e.out1) + (row * e.ld0 + col) * 2;
-                a.o2 = static_cast<char*>(e.out2) + (row * e.ld0 + col) * 2;
-            } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-                a.o1 = a.o0 + e.nsplit * 2;
-                a.i0 = static_cast<const char*>(e.in0) + (row * e.ldi0 + col) * 2;
-                a.i1 = static_cast<const char*>(e.in1) + (row * e.ldi0 + col) * 2;
-                a.o2 = e.out2 ? static_cast<char*>(e.out2) + (row * e.ldi0 + col) * 2 : nullptr;
-            } else if constexpr (EPI == EPI_RESID) {
-                a.i0 = static_cast<const char*>(e.in0) + (row * e.ldi0 + col) * 2;
-            }
         }
         return a;
     };
@@ -526,21 +789,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
                     const float v[4] = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
                     quad_transpose(v, w[j], (jq & 1) != 0, (jq & 2) != 0);
                 }
-                if constexpr (EPI == EPI_SWIGLU) {
-                    // a wavefront's 64 B rows are 32 gate rows then 32 up rows
-                    // of the same 32 hidden columns
-                    if (ok(i, q, 0)) epi4_swiglu(ptr(i, q, 0), w[0], w[1]);
-                } else {
 #pragma clang loop unroll(full)
-                    for (int j = 0; j < 2; ++j)
-                        if (ok(i, q, j)) epi4<EPI>(ptr(i, q, j), w[j], in[i % (PD + 1)][q][j]);
-                }
+                for (int j = 0; j < 2; ++j)
+                    if (ok(i, q, j)) epi4<EPI>(ptr(i, q, j), w[j], in[i % (PD + 1)][q][j]);
             }
         }
     };
     if (fast) run(std::true_type{});
     else run(std::false_type{});
 }
+
 
 // Byte extent of a row-major operand: (rows-1)*ld + cols elements of bf16.
 inline bool extent(int64_t rows, int64_t ld, int64_t cols, uint32_t& out) {
@@ -550,9 +808,15 @@ inline bool extent(int64_t rows, int64_t ld, int64_t cols, uint32_t& out) {
     return true;
 }
 
-template <int EPI, bool MN = false>
+template <int EPI>
 hipError_t launch(const Params& p, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_tn_kernel<EPI, MN>), dim3(p.tiles_m * p.tiles_n), dim3(NTHREADS), 0, s, p);
+    hipLaunchKernelGGL((gemm_tn_kernel<EPI>), dim3(p.tiles_m * p.tiles_n), dim3(NTHREADS), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_mn(const Params& p, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_mn_kernel<EPI>), dim3(p.tiles_m * p.tiles_n), dim3(MN_THREADS), 0, s, p);
     return hipGetLastError();
 }
 
@@ -593,7 +857,7 @@ hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
     }
     p.e = a.e;
     if (p.tiles_m == 0 || p.tiles_n == 0) return hipSuccess;
-    if (mn) return a.epi == EPI_ACC_F32 ? launch<EPI_ACC_F32, true>(p, s) : launch<EPI_STORE_F32, true>(p, s);
+    if (mn) return a.epi == EPI_ACC_F32 ? launch_mn<EPI_ACC_F32>(p, s) : launch_mn<EPI_STORE_F32>(p, s);
     switch (a.epi) {
         case EPI_SWIGLU: return launch<EPI_SWIGLU>(p, s);
         case EPI_RESID: return launch<EPI_RESID>(p, s);
