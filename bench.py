@@ -36,10 +36,10 @@ PEAK_HBM_GBS = 8000.0
 # copy kernel measured in the same runs).  Valid only for the GEMM source they were taken on.
 TRAFFIC = {
     "config": "c3_80layer_p8_stage0",
-    "gemm_source_sha1": "5219b769c10f2d6893a4cbe3830f82ddcca68410",
+    "gemm_source_sha1": "6394cc73bc01519240ce07b0620e02cbd6b7d9b0",
     "bytes_per_launch": {
-        "gemm_gateup_swiglu": 14.44e9, "gemm_down_residual": 5.907e9, "gemm_dh_swiglu_bwd": 8.533e9,
-        "gemm_dn": 11.64e9, "gemm_wgrad_down": 7.516e9, "gemm_wgrad_gateup": 15.08e9,
+        "gemm_gateup_swiglu": 16.96e9, "gemm_down_residual": 6.194e9, "gemm_dh_swiglu_bwd": 8.777e9,
+        "gemm_dn": 13.37e9, "gemm_wgrad_down": 7.55e9, "gemm_wgrad_gateup": 15.18e9,
     },
 }
 
