@@ -223,6 +223,73 @@ __device__ __forceinline__ void epi4_swiglu(const EpiPtr& a, const float (&g)[4]
     *reinterpret_cast<uint2*>(a.o2) = pack4(hh);
 }
 
+// Eight consecutive output columns of one row (the K-contiguous kernel's
+// accumulator layout): 16-byte bf16 and 32-byte fp32 accesses.
+__device__ __forceinline__ uint4 pack8(const float (&w)[8]) {
+    return make_uint4(pack2_bf(w[0], w[1]), pack2_bf(w[2], w[3]), pack2_bf(w[4], w[5]), pack2_bf(w[6], w[7]));
+}
+
+__device__ __forceinline__ void unpack8(uint4 q, float (&w)[8]) {
+    const uint32_t v[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        w[2 * k] = bf2f(v[k] & 0xffffu);
+        w[2 * k + 1] = bf2f(v[k] >> 16);
+    }
+}
+
+template <int EPI> struct EpiIn8 {};
+template <> struct EpiIn8<EPI_RESID> { uint4 x; };
+template <> struct EpiIn8<EPI_SWIGLU_BWD> { uint4 g, u; };
+template <> struct EpiIn8<EPI_ACC_F32> { float4 c0, c1; };
+
+template <int EPI>
+__device__ __forceinline__ void epi_load8(const EpiPtr& a, EpiIn8<EPI>& in) {
+    if constexpr (EPI == EPI_RESID) {
+        in.x = *reinterpret_cast<const uint4*>(a.i0);
+    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+        in.g = *reinterpret_cast<const uint4*>(a.i0);
+        in.u = *reinterpret_cast<const uint4*>(a.i1);
+    } else if constexpr (EPI == EPI_ACC_F32) {
+        in.c0 = reinterpret_cast<const float4*>(a.i0)[0];
+        in.c1 = reinterpret_cast<const float4*>(a.i0)[1];
+    }
+}
+
+template <int EPI>
+__device__ __forceinline__ void epi8(const EpiPtr& a, const float (&w)[8], const EpiIn8<EPI>& in) {
+    if constexpr (EPI == EPI_STORE_F32) {
+        reinterpret_cast<float4*>(a.o0)[0] = make_float4(w[0], w[1], w[2], w[3]);
+        reinterpret_cast<float4*>(a.o0)[1] = make_float4(w[4], w[5], w[6], w[7]);
+    } else if constexpr (EPI == EPI_STORE) {
+        *reinterpret_cast<uint4*>(a.o0) = pack8(w);
+    } else if constexpr (EPI == EPI_RESID) {
+        float x[8], y[8];
+        unpack8(in.x, x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = x[k] + w[k];
+        *reinterpret_cast<uint4*>(a.o0) = pack8(y);
+    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+        float g[8], u[8], dg[8], du[8];
+        unpack8(in.g, g);
+        unpack8(in.u, u);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) swiglu_bwd_f(w[k], g[k], u[k], dg[k], du[k]);
+        *reinterpret_cast<uint4*>(a.o0) = pack8(dg);
+        *reinterpret_cast<uint4*>(a.o1) = pack8(du);
+        if (a.o2) {   // optional h = silu(g) u, as the forward computed it
+            float hh[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) hh[k] = swiglu_f(g[k], u[k]);
+            *reinterpret_cast<uint4*>(a.o2) = pack8(hh);
+        }
+    } else if constexpr (EPI == EPI_ACC_F32) {
+        const float4 c0 = in.c0, c1 = in.c1;
+        reinterpret_cast<float4*>(a.o0)[0] = make_float4(c0.x + w[0], c0.y + w[1], c0.z + w[2], c0.w + w[3]);
+        reinterpret_cast<float4*>(a.o0)[1] = make_float4(c1.x + w[4], c1.y + w[5], c1.z + w[6], c1.w + w[7]);
+    }
+}
+
 // s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt left at its maximum).
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
@@ -279,6 +346,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     rsrc_t ar, br;
     int64_t K = 0;
     int nk = 0;
+    // B rows go to LDS permuted within each wavefront's 128 rows: LDS row
+    // 16j + c (MFMA tile j, column c) holds B row 8c + j, so a lane's eight
+    // accumulators of one row are eight consecutive output columns.  SwiGLU
+    // (B rows interleaved in groups of 32 gate and 32 up rows): tiles j < 4
+    // hold gate row of hidden column 4c + j, tiles j >= 4 the up row of
+    // hidden column 4c + j - 4.
+    auto brow = [&](int row) __attribute__((always_inline)) -> int {
+        const int blk = row & ~127, j = (row >> 4) & 7, c = row & 15;
+        if (!p.swiglu) return blk + 8 * c + j;
+        const int x = 4 * c + (j & 3);
+        return blk + (x >> 5) * 64 + (j >> 2) * 32 + (x & 31);
+    };
     auto set_seg = [&](int s) __attribute__((always_inline)) {
         const Seg g = s == 0 ? p.seg[0] : p.seg[1];   // no dynamic index into the arguments
         ar = make_rsrc(g.A, g.a_bytes);
@@ -288,7 +367,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int row = (wave * NQ + q) * 8 + (lane >> 3);
-            const int64_t ra = m0 + row, rb = nb0 + row;
+            const int64_t ra = m0 + row, rb = nb0 + brow(row);
             aoff[q] = ra < p.M ? (uint32_t)(ra * g.lda * 2 + lcq[q] * 16) : OOB;
             boff[q] = rb < p.NB ? (uint32_t)(rb * g.ldb * 2 + lcq[q] * 16) : OOB;
         }
@@ -422,22 +501,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         __builtin_amdgcn_s_barrier();
     }
 
-    // Epilogue on quad-transposed accumulators: this lane owns tile row
-    // lr + 16i and tile columns lc + 16j .. +3 (SwiGLU: hidden columns lc +
-    // 16jj from the gate tile {0,1,4,5}[jj] and the up tile two further).
-    const int jq = lane & 3;
-    const int lr = wm * 128 + 4 * (lane >> 4) + jq;
-    const int lc = (p.swiglu ? wn * 64 : wn * 128) + 4 * ((lane >> 2) & 3);
+    // Epilogue.  With the permuted B rows, accumulator register r of tile
+    // (i, j) is output row lr + 16i + r, column lc + j: each lane holds eight
+    // consecutive columns of a row (SwiGLU: gate tiles j < 4 and up tiles
+    // j >= 4 of the four hidden columns lc .. lc+3).
+    const int lr = wm * 128 + 4 * (lane >> 4);
+    const int lc = p.swiglu ? wn * 64 + 4 * (lane & 15) : wn * 128 + 8 * (lane & 15);
     const EpiArgs e = p.e;
     const int64_t pM = p.M, pN = p.N;
     constexpr int ESO = (EPI == EPI_STORE_F32 || EPI == EPI_ACC_F32) ? 4 : 2;   // output element bytes
     constexpr bool HAS_IN = EPI == EPI_RESID || EPI == EPI_SWIGLU_BWD || EPI == EPI_ACC_F32;
-    constexpr int PD = 1;   // row groups loaded ahead
-    EpiIn<EPI> in[PD + 1][8];
 
     // Whole tile inside M x N (and, for the split fp32 accumulate, on one side
     // of nsplit): every operand is a uniform per-tile base plus this lane's
-    // fixed 32-bit offset plus a uniform per-(i, j) offset, so the accesses
+    // fixed 32-bit offset plus a uniform per-(i, r) offset, so the accesses
     // need no bounds checks and no per-element 64-bit index arithmetic.
     bool fast = m0 + BM <= pM && n0 + (p.swiglu ? BN / 2 : BN) <= pN;
     char* ob = nullptr;            // output tile base
@@ -454,10 +531,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     } else {
         ob = static_cast<char*>(e.out0) + (m0 * e.ld0 + n0) * ESO;
     }
+
     const uint32_t lo = (uint32_t)(((int64_t)lr * old + lc) * ESO);
     const uint32_t li = (uint32_t)(((int64_t)lr * e.ldi0 + lc) * 2);
-    auto fptr = [&](int i, int j) __attribute__((always_inline)) -> EpiPtr {
-        const int64_t uo = ((int64_t)(i * 16) * old + j * 16) * ESO;
+    auto fptr = [&](int i, int r) __attribute__((always_inline)) -> EpiPtr {
+        const int64_t uo = (int64_t)(i * 16 + r) * old * ESO;
         EpiPtr a{};
         char* o = ob + uo + lo;
         a.o0 = o;
@@ -466,18 +544,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
             a.o2 = static_cast<char*>(e.out2) + (m0 * e.ld0 + n0) * 2 + uo + lo;
         } else if constexpr (EPI == EPI_SWIGLU_BWD) {
             a.o1 = o + e.nsplit * 2;
-            const int64_t ui = ((int64_t)(i * 16) * e.ldi0 + j * 16 + m0 * e.ldi0 + n0) * 2;
+            const int64_t ui = ((int64_t)(i * 16 + r) * e.ldi0 + m0 * e.ldi0 + n0) * 2;
             a.i0 = static_cast<const char*>(e.in0) + ui + li;
             a.i1 = static_cast<const char*>(e.in1) + ui + li;
             a.o2 = e.out2 ? static_cast<char*>(e.out2) + ui + li : nullptr;
         } else if constexpr (EPI == EPI_RESID) {
-            const int64_t ui = ((int64_t)(i * 16) * e.ldi0 + j * 16 + m0 * e.ldi0 + n0) * 2;
-            a.i0 = static_cast<const char*>(e.in0) + ui + li;
+            a.i0 = static_cast<const char*>(e.in0) + ((int64_t)(i * 16 + r) * e.ldi0 + m0 * e.ldi0 + n0) * 2 + li;
         } else if constexpr (EPI == EPI_ACC_F32) {
             a.i0 = o;
         }
         return a;
     };
+    // edge tiles: the same accesses from (row, col); a column group lies
+    // wholly inside or outside N and on one side of nsplit (multiples of 8)
     auto sptr = [&](int64_t row, int64_t col) __attribute__((always_inline)) -> EpiPtr {
         EpiPtr a{};
         if constexpr (EPI == EPI_ACC_F32) {
@@ -501,46 +580,40 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         return a;
     };
 
-    constexpr int NJ = EPI == EPI_SWIGLU ? 4 : 8;   // column groups per row group
     auto run = [&](auto fast_c) __attribute__((always_inline)) {
         constexpr bool FAST = decltype(fast_c)::value;
-        auto ptr = [&](int i, int j) __attribute__((always_inline)) -> EpiPtr {
-            if constexpr (FAST) return fptr(i, j);
-            else return sptr(m0 + lr + i * 16, n0 + lc + j * 16);
+        auto ptr = [&](int i, int r) __attribute__((always_inline)) -> EpiPtr {
+            if constexpr (FAST) return fptr(i, r);
+            else return sptr(m0 + lr + i * 16 + r, n0 + lc);
         };
-        auto ok = [&](int i, int j) __attribute__((always_inline)) -> bool {
+        auto ok = [&](int i, int r) __attribute__((always_inline)) -> bool {
             if constexpr (FAST) return true;
-            else return m0 + lr + i * 16 < pM && n0 + lc + j * 16 < pN;
+            else return m0 + lr + i * 16 + r < pM && n0 + lc < pN;
         };
-        auto prefetch = [&](int i, EpiIn<EPI> (&dst)[8]) __attribute__((always_inline)) {
+        // inputs of row group i + 1 load while row group i computes
+        EpiIn8<EPI> in[2][4];
+        auto prefetch = [&](int i, EpiIn8<EPI> (&dst)[4]) __attribute__((always_inline)) {
             if constexpr (HAS_IN) {
-#pragma clang loop unroll(full)
-                for (int j = 0; j < NJ; ++j)
-                    if (ok(i, j)) epi_load<EPI>(ptr(i, j), dst[j]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (ok(i, r)) epi_load8<EPI>(ptr(i, r), dst[r]);
             }
         };
-        auto tr = [&](int i, int j, float (&w)[4]) __attribute__((always_inline)) {
-            const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-            quad_transpose(v, w, (jq & 1) != 0, (jq & 2) != 0);
-        };
-#pragma clang loop unroll(full)
-        for (int i = 0; i < PD; ++i) prefetch(i, in[i]);
-#pragma clang loop unroll(full)
+        prefetch(0, in[0]);
+#pragma unroll
         for (int i = 0; i < 8; ++i) {
-            if (i + PD < 8) prefetch(i + PD, in[(i + PD) % (PD + 1)]);
-#pragma clang loop unroll(full)
-            for (int j = 0; j < NJ; ++j) {
+            if (i + 1 < 8) prefetch(i + 1, in[(i + 1) & 1]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
                 if constexpr (EPI == EPI_SWIGLU) {
-                    // B rows of a wavefront: 32 gate, 32 up, 32 gate, 32 up rows
-                    const int gj = (j >> 1) * 4 + (j & 1);
-                    float g[4], u[4];
-                    tr(i, gj, g);
-                    tr(i, gj + 2, u);
-                    if (ok(i, j)) epi4_swiglu(ptr(i, j), g, u);
+                    const float g[4] = {acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
+                    const float u[4] = {acc[i][4][r], acc[i][5][r], acc[i][6][r], acc[i][7][r]};
+                    if (ok(i, r)) epi4_swiglu(ptr(i, r), g, u);
                 } else {
-                    float w[4];
-                    tr(i, j, w);
-                    if (ok(i, j)) epi4<EPI>(ptr(i, j), w, in[i % (PD + 1)][j]);
+                    float w[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) w[j] = acc[i][j][r];
+                    if (ok(i, r)) epi8<EPI>(ptr(i, r), w, in[i & 1][r]);
                 }
             }
         }
@@ -833,6 +906,19 @@ hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
     const bool mn = !a.a_kcontig;
     if (a.b_kcontig == mn) return hipErrorInvalidValue;
     if (mn && (a.swiglu_map || (a.epi != EPI_STORE_F32 && a.epi != EPI_ACC_F32))) return hipErrorInvalidValue;
+    // the K-contiguous epilogue moves 8 consecutive output columns (SwiGLU: 4
+    // hidden columns) with 16-byte accesses
+    if (!mn) {
+        const bool in = a.epi == EPI_RESID || a.epi == EPI_SWIGLU_BWD;
+        const bool split = a.epi == EPI_SWIGLU_BWD || a.epi == EPI_ACC_F32;
+        if (a.N % 8 || a.e.ld0 % 8 || (in && a.e.ldi0 % 8) || (split && a.e.nsplit % 8) ||
+            (a.epi == EPI_ACC_F32 && a.e.ld1 % 8))
+            return hipErrorInvalidValue;
+        const uintptr_t ptrs = reinterpret_cast<uintptr_t>(a.e.out0) | reinterpret_cast<uintptr_t>(a.e.out1) |
+                               reinterpret_cast<uintptr_t>(a.e.out2) | reinterpret_cast<uintptr_t>(a.e.in0) |
+                               reinterpret_cast<uintptr_t>(a.e.in1);
+        if (ptrs % 16) return hipErrorInvalidValue;
+    }
     Params p{};
     p.M = a.M;
     p.N = a.N;
