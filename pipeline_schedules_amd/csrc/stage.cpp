@@ -74,6 +74,10 @@ struct pps_stage {
     bool ac = false;
     size_t s_rc = 0;
     size_t s_n = 0, s_h = 0, s_dgu = 0, s_dn = 0, s_dxa = 0, s_dxb = 0, s_part = 0, s_dz = 0;
+    // bf16 weight gradients: T-contiguous copies of h, n, dy and dg|du
+    // ([features, Tp], Tp = T rounded up to 8, zero-padded)
+    size_t s_hT = 0, s_nT = 0, s_dyT = 0, s_dguT = 0;
+    int64_t Tp = 0;
     bool tn = false;                  // bf16 path: the forward GEMMs read K-contiguous weight copies
     // bf16 path: per-pass copies of the forward weights, [chunk*L + block]:
     // WguT (swiglu_b_rows(ffn) x d, gate/up interleaved per 32) and WdT (d x ffn)
@@ -322,8 +326,9 @@ int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_
 }
 
 // Weight gradient of block b: dWd += h^T dy; dWg += n^T dg; dWu += n^T du.
-// Every operand is read as stored, [T, features] (the GEMMs reduce over the
-// T rows).  n and h are in the scratch buffers when `have_nh` (the backward
+// The GEMMs reduce over the T rows.  bf16: the operands are first copied
+// T-contiguous ([features, T]) for the K-contiguous kernel; fp32 reads them as
+// stored.  n and h are in the scratch buffers when `have_nh` (the backward
 // just produced them); otherwise they are recomputed from the stash.
 int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, const void* dgu, bool have_nh) {
     const pps_stage_desc& D = h->d;
@@ -349,12 +354,31 @@ int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, cons
     a.M = f; a.N = d; a.nseg = 1;
     a.seg[0].A = sh; a.seg[0].lda = f; a.seg[0].B = dy; a.seg[0].ldb = d; a.seg[0].K = T;
     a.a_kcontig = false; a.b_kcontig = false;
-    a.epi = pps::EPI_ACC_F32;
-    a.e.out0 = dWd; a.e.ld0 = d; a.e.nsplit = d;
-    PPS_TRY(timed(h, PPS_K_WGRAD_DOWN, gemm_flops(f, d, T), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
     c.M = d; c.N = 2 * f; c.nseg = 1;
     c.seg[0].A = sn; c.seg[0].lda = d; c.seg[0].B = dgu; c.seg[0].ldb = 2 * f; c.seg[0].K = T;
     c.a_kcontig = false; c.b_kcontig = false;
+    if (h->tn) {
+        const int64_t Tp = h->Tp;
+        char* hT = h->scratch + h->s_hT;
+        char* nT = h->scratch + h->s_nT;
+        char* dyT = h->scratch + h->s_dyT;
+        char* dguT = h->scratch + h->s_dguT;
+        auto tr = [&](const void* src, int64_t cols, void* dst) {
+            return timed(h, PPS_K_COPY, 0.0, 2.0 * T * cols * 2, [&] {
+                return pps::transpose_bf16(src, T, cols, cols, dst, Tp, 0, 0, h->stream);
+            });
+        };
+        PPS_TRY(tr(sh, f, hT));
+        PPS_TRY(tr(dy, d, dyT));
+        PPS_TRY(tr(sn, d, nT));
+        PPS_TRY(tr(dgu, 2 * f, dguT));
+        a.seg[0].A = hT; a.seg[0].lda = Tp; a.seg[0].B = dyT; a.seg[0].ldb = Tp;
+        c.seg[0].A = nT; c.seg[0].lda = Tp; c.seg[0].B = dguT; c.seg[0].ldb = Tp;
+        a.a_kcontig = a.b_kcontig = c.a_kcontig = c.b_kcontig = true;
+    }
+    a.epi = pps::EPI_ACC_F32;
+    a.e.out0 = dWd; a.e.ld0 = d; a.e.nsplit = d;
+    PPS_TRY(timed(h, PPS_K_WGRAD_DOWN, gemm_flops(f, d, T), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
     c.epi = pps::EPI_ACC_F32;
     c.e.out0 = dWg; c.e.ld0 = f; c.e.out1 = dWu; c.e.ld1 = f; c.e.nsplit = f;
     PPS_TRY(timed(h, PPS_K_WGRAD_GATEUP, gemm_flops(d, 2.0 * f, T), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
@@ -584,6 +608,12 @@ extern "C" int pps_stage_create(const pps_stage_desc* desc, pps_stage** out) {
         take(h->s_dn, T * dm * 4);
         take(h->s_part, (size_t)pps::rmsnorm_bwd_partial_rows((int64_t)T) * dm * 4);
         if (h->tn) {
+            h->Tp = (desc->T + 7) / 8 * 8;
+            const size_t Tp = (size_t)h->Tp;
+            take(h->s_hT, f * Tp * 2);
+            take(h->s_nT, dm * Tp * 2);
+            take(h->s_dyT, dm * Tp * 2);
+            take(h->s_dguT, 2 * f * Tp * 2);
             size_t w = 0;
             for (int i = 0; i < desc->v * desc->L; ++i) {
                 h->wgu_off.push_back(w);
