@@ -158,7 +158,7 @@ def main():
     ops = pps.make_schedule(cfg.P, cfg.M, cfg.k, cfg.v, kind_id)
     launches_per_pass = 0
     per_block_f = 3 if cfg.block == "swiglu" else 2
-    per_block_b = 11 if cfg.block == "swiglu" else 5   # bf16 SwiGLU: 4 transposed copies for dW
+    per_block_b = 12 if cfg.block == "swiglu" else 5   # bf16 SwiGLU: 4 transposed copies, dW_g and dW_u apart
     launches_per_pass = cfg.M * cfg.v * cfg.L * (per_block_f + per_block_b) + 2 * cfg.M * cfg.v
     flags = 0 if args.no_profile else pps.FLAG_PROFILE
     if args.recompute:

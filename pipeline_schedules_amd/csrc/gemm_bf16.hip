@@ -512,25 +512,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     constexpr int ESO = (EPI == EPI_STORE_F32 || EPI == EPI_ACC_F32) ? 4 : 2;   // output element bytes
     constexpr bool HAS_IN = EPI == EPI_RESID || EPI == EPI_SWIGLU_BWD || EPI == EPI_ACC_F32;
 
-    // Whole tile inside M x N (and, for the split fp32 accumulate, on one side
-    // of nsplit): every operand is a uniform per-tile base plus this lane's
-    // fixed 32-bit offset plus a uniform per-(i, r) offset, so the accesses
-    // need no bounds checks and no per-element 64-bit index arithmetic.
-    bool fast = m0 + BM <= pM && n0 + (p.swiglu ? BN / 2 : BN) <= pN;
-    char* ob = nullptr;            // output tile base
-    int64_t old = e.ld0;           // its leading dimension (elements)
-    if constexpr (EPI == EPI_ACC_F32) {
-        if (n0 + BN <= e.nsplit) {
-            ob = static_cast<char*>(e.out0) + (m0 * e.ld0 + n0) * 4;
-        } else if (n0 >= e.nsplit) {
-            ob = static_cast<char*>(e.out1) + (m0 * e.ld1 + (n0 - e.nsplit)) * 4;
-            old = e.ld1;
-        } else {
-            fast = false;
-        }
-    } else {
-        ob = static_cast<char*>(e.out0) + (m0 * e.ld0 + n0) * ESO;
-    }
+    // Whole tile inside M x N: every operand is a uniform per-tile base plus
+    // this lane's fixed 32-bit offset plus a uniform per-(i, r) offset, so the
+    // accesses need no bounds checks and no per-element 64-bit index
+    // arithmetic.  (The fp32 accumulate here writes out0 only.)
+    const bool fast = m0 + BM <= pM && n0 + (p.swiglu ? BN / 2 : BN) <= pN;
+    char* const ob = static_cast<char*>(e.out0) + (m0 * e.ld0 + n0) * ESO;   // output tile base
+    const int64_t old = e.ld0;                                               // its leading dimension
 
     const uint32_t lo = (uint32_t)(((int64_t)lr * old + lc) * ESO);
     const uint32_t li = (uint32_t)(((int64_t)lr * e.ldi0 + lc) * 2);
@@ -556,15 +544,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         return a;
     };
     // edge tiles: the same accesses from (row, col); a column group lies
-    // wholly inside or outside N and on one side of nsplit (multiples of 8)
+    // wholly inside or outside N (a multiple of 8)
     auto sptr = [&](int64_t row, int64_t col) __attribute__((always_inline)) -> EpiPtr {
         EpiPtr a{};
+        a.o0 = static_cast<char*>(e.out0) + (row * e.ld0 + col) * ESO;
         if constexpr (EPI == EPI_ACC_F32) {
-            float* c = acc_ptr(e, row, col);
-            a.o0 = reinterpret_cast<char*>(c);
-            a.i0 = reinterpret_cast<const char*>(c);
+            a.i0 = a.o0;
         } else {
-            a.o0 = static_cast<char*>(e.out0) + (row * e.ld0 + col) * ESO;
             if constexpr (EPI == EPI_SWIGLU) {
                 a.o1 = static_cast<char*>(e.out1) + (row * e.ld0 + col) * 2;
                 a.o2 = static_cast<char*>(e.out2) + (row * e.ld0 + col) * 2;
@@ -910,10 +896,9 @@ hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
     // hidden columns) with 16-byte accesses
     if (!mn) {
         const bool in = a.epi == EPI_RESID || a.epi == EPI_SWIGLU_BWD;
-        const bool split = a.epi == EPI_SWIGLU_BWD || a.epi == EPI_ACC_F32;
-        if (a.N % 8 || a.e.ld0 % 8 || (in && a.e.ldi0 % 8) || (split && a.e.nsplit % 8) ||
-            (a.epi == EPI_ACC_F32 && a.e.ld1 % 8))
+        if (a.N % 8 || a.e.ld0 % 8 || (in && a.e.ldi0 % 8) || (a.epi == EPI_SWIGLU_BWD && a.e.nsplit % 8))
             return hipErrorInvalidValue;
+        if (a.epi == EPI_ACC_F32 && a.e.nsplit < a.N) return hipErrorInvalidValue;   // out0 only
         const uintptr_t ptrs = reinterpret_cast<uintptr_t>(a.e.out0) | reinterpret_cast<uintptr_t>(a.e.out1) |
                                reinterpret_cast<uintptr_t>(a.e.out2) | reinterpret_cast<uintptr_t>(a.e.in0) |
                                reinterpret_cast<uintptr_t>(a.e.in1);

@@ -22,6 +22,7 @@ enum Epi {
     EPI_SWIGLU_BWD = 3,  // dh=acc; g=in0,u=in1 (ldi0) -> out0[m*ld0+n]=dg, out0[..+nsplit]=du,
                          // and if out2: out2[m*ldi0+n] = h = silu(g) u
     EPI_ACC_F32 = 4,     // n <  nsplit: out0[m*ld0+n] += acc; else out1[m*ld1+n-nsplit] += acc
+                         // (bf16 K-contiguous operands: out0 only, nsplit >= N)
     EPI_BIAS_GELU = 5,   // z = acc + bias[n]; out0 = z, out1 = GELU(z)   (fp32 only)
     EPI_STORE = 6,       // out0[m*ld0+n] = acc                           (storage type)
 };

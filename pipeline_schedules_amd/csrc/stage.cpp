@@ -380,6 +380,17 @@ int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, cons
     a.e.out0 = dWd; a.e.ld0 = d; a.e.nsplit = d;
     PPS_TRY(timed(h, PPS_K_WGRAD_DOWN, gemm_flops(f, d, T), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
     c.epi = pps::EPI_ACC_F32;
+    if (h->tn) {
+        // the K-contiguous kernel accumulates into one output: dW_g, then dW_u
+        // from the second half of dg|du's rows
+        c.N = f;
+        c.e.out0 = dWg; c.e.ld0 = f; c.e.nsplit = f;
+        PPS_TRY(timed(h, PPS_K_WGRAD_GATEUP, gemm_flops(d, f, T), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
+        c.seg[0].B = static_cast<const char*>(c.seg[0].B) + (size_t)f * h->Tp * 2;
+        c.e.out0 = dWu;
+        PPS_TRY(timed(h, PPS_K_WGRAD_GATEUP, gemm_flops(d, f, T), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
+        return PPS_OK;
+    }
     c.e.out0 = dWg; c.e.ld0 = f; c.e.out1 = dWu; c.e.ld1 = f; c.e.nsplit = f;
     PPS_TRY(timed(h, PPS_K_WGRAD_GATEUP, gemm_flops(d, 2.0 * f, T), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
     return PPS_OK;
