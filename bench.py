@@ -36,10 +36,10 @@ PEAK_HBM_GBS = 8000.0
 # copy kernel measured in the same runs).  Valid only for the GEMM source they were taken on.
 TRAFFIC = {
     "config": "c3_80layer_p8_stage0",
-    "gemm_source_sha1": "2146c0570872dc44212069a361eb5f0c82442610",
+    "gemm_source_sha1": "f1d459bac5b4dfa9a5d41dc8228b3311a6e03d65",
     "bytes_per_launch": {
-        "gemm_gateup_swiglu": 13.21e9, "gemm_down_residual": 6.016e9, "gemm_dh_swiglu_bwd": 8.660e9,
-        "gemm_dn": 12.72e9, "gemm_wgrad_down": 7.554e9, "gemm_wgrad_gateup": 15.39e9,
+        "gemm_gateup_swiglu": 13.59e9, "gemm_down_residual": 6.002e9, "gemm_dh_swiglu_bwd": 8.802e9,
+        "gemm_dn": 12.86e9, "gemm_wgrad_down": 8.452e9, "gemm_wgrad_gateup": 8.452e9,
     },
 }
 

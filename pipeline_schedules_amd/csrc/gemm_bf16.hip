@@ -1,17 +1,15 @@
 // bf16 GEMM on the CDNA4 matrix cores (gfx950), fp32 accumulation.
 //
-// Layouts: C[m,n] = sum_k A(m,k) B(n,k) with both operands either
-//   K-contiguous ("TN"): A row-major [M, K] (stride lda), B [N, K] (ldb), or
-//   M/N-contiguous ("MN"): A row-major [K, M] (stride lda), B [K, N] (ldb).
-// The forward and input-gradient GEMMs run TN (the forward reads per-pass
-// K-contiguous copies of the weights); the weight-gradient GEMMs dW = X^T Y
-// reduce over tokens and read the activations and gradients as they are
-// stored, [T, features], in the MN mode, which needs no transposed copies.
-// Both kernels tile 256 x 256 x 64, take both operands straight from memory
-// into LDS (direct-to-LDS buffer loads, no register staging) and read zeros
-// outside an operand's extent, which pads ragged M, N and K tails.
+// Layout: C[m,n] = sum_k A(m,k) B(n,k) with both operands K-contiguous
+// ("TN"): A row-major [M, K] (stride lda), B [N, K] (ldb).  The forward reads
+// per-pass K-contiguous copies of the weights; the weight-gradient GEMMs
+// dW = X^T Y reduce over tokens and read T-contiguous copies of the
+// activations and gradients.  The kernel tiles 256 x 256 x 64, takes both
+// operands straight from memory into LDS (direct-to-LDS buffer loads, no
+// register staging) and reads zeros outside an operand's extent, which pads
+// ragged M, N and K tails.
 //
-// TN kernel: 256 threads = 4 wavefronts in a 2 x 2 grid, one per SIMD,
+// Kernel: 256 threads = 4 wavefronts in a 2 x 2 grid, one per SIMD,
 // 128 x 128 per wavefront = 8 x 8 tiles of v_mfma_f32_16x16x32_bf16 (256
 // fp32 accumulators per lane, in AGPRs).  LDS holds a ring of five 32 KB
 // operand-tile slots, A of K tile t in slot 2t mod 5 and B in slot 2t+1 mod 5.
@@ -37,10 +35,6 @@
 // K tail live in a separate tail loop, which leaves one M0 write per load and
 // the LDS reads between the MFMAs.
 //
-// MN kernel (weight gradients): 8 wavefronts of 128 x 64 with
-// v_mfma_f32_32x32x16_bf16 and transposing LDS reads (ds_read_b64_tr_b16);
-// it is described where it is defined.
-//
 // Workgroup -> tile mapping: the dispatcher places workgroup i on XCD i % 8;
 // ids are remapped so each XCD gets a contiguous run of logical tiles, and
 // logical tiles are ordered in groups of 8 tile-rows so the tiles running on
@@ -53,17 +47,13 @@ namespace pps {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int NTHREADS = 256;            // TN kernel: 4 wavefronts
-constexpr int MN_THREADS = 512;          // M/N-contiguous kernel: 8 wavefronts
-constexpr int NQ = 8;                    // TN: 1 KB load pieces per wavefront per operand tile
+constexpr int NTHREADS = 256;            // 4 wavefronts
+constexpr int NQ = 8;                    // 1 KB load pieces per wavefront per operand tile
 constexpr int ROWB = BK * 2;             // TN: 128 bytes per LDS row
 constexpr int OPB = 256 * ROWB;          // 32 KB per operand tile
 constexpr int NSLOT = 5;                 // operand-tile slots
@@ -104,34 +94,10 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
 }
 
 // ---- epilogue ---------------------------------------------------------------
-// A 16x16 MFMA accumulator gives lane l column l%16 and rows 4*(l/16) + 0..3;
-// a 32x32 one column l%32 and, for element group q, rows q*8 + 4*(l/32) +
-// 0..3.  A 4x4 transpose inside each lane quad (DPP quad permutes) gives each
-// lane one row and four consecutive columns, so every global access of the
-// epilogue is an 8-byte (bf16) or 16-byte (fp32) vector.
-
-template <int CTRL>
-__device__ __forceinline__ float quad_xor(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// 4x4 transpose across a lane quad in two butterfly rounds.  In: lane j holds
-// column j (v[r] = M[r][j]); out: lane j holds row j (w[m] = M[j][m]).  Round
-// one swaps the odd/even elements with lane j^1, round two the element pairs
-// with lane j^2; o1 and o2 are the lane's bits 0 and 1.
-__device__ __forceinline__ void quad_transpose(const float (&v)[4], float (&w)[4], bool o1, bool o2) {
-    float a = o1 ? v[0] : v[1], b = o1 ? v[2] : v[3];
-    a = quad_xor<0xB1>(a);
-    b = quad_xor<0xB1>(b);
-    const float x0 = o1 ? a : v[0], x1 = o1 ? v[1] : a, x2 = o1 ? b : v[2], x3 = o1 ? v[3] : b;
-    float c = o2 ? x0 : x2, d = o2 ? x1 : x3;
-    c = quad_xor<0x4E>(c);
-    d = quad_xor<0x4E>(d);
-    w[0] = o2 ? c : x0;
-    w[1] = o2 ? d : x1;
-    w[2] = o2 ? x2 : c;
-    w[3] = o2 ? x3 : d;
-}
+// A 16x16 MFMA accumulator gives lane l column l%16 and rows 4*(l/16) + 0..3.
+// With B's rows permuted at load time (see the loader) the columns of a
+// lane's eight tiles j are consecutive output columns, so each lane owns
+// 8-column pieces of rows and every global access is a 16-byte vector.
 
 __device__ __forceinline__ uint2 pack4(const float (&w)[4]) {
     return make_uint2(pack2_bf(w[0], w[1]), pack2_bf(w[2], w[3]));
@@ -142,20 +108,7 @@ __device__ __forceinline__ void unpack4(uint2 q, float (&w)[4]) {
     w[2] = bf2f(q.y & 0xffffu); w[3] = bf2f(q.y >> 16);
 }
 
-// Inputs an epilogue reads for four consecutive output columns.  They are
-// loaded one row group ahead of their use so the loads overlap the math.
-template <int EPI> struct EpiIn {};
-template <> struct EpiIn<EPI_RESID> { uint2 x; };
-template <> struct EpiIn<EPI_SWIGLU_BWD> { uint2 g, u; };
-template <> struct EpiIn<EPI_ACC_F32> { float4 c; };
-
-__device__ __forceinline__ float* acc_ptr(const EpiArgs& e, int64_t row, int64_t col) {
-    return col < e.nsplit ? static_cast<float*>(e.out0) + row * e.ld0 + col
-                          : static_cast<float*>(e.out1) + row * e.ld1 + (col - e.nsplit);
-}
-
-// The epilogue's memory operands for four consecutive output columns of one
-// row: i0/i1 the inputs read, o0/o1/o2 the outputs written (which ones a role
+// The epilogue's memory operands for consecutive output columns of one row: i0/i1 the inputs read, o0/o1/o2 the outputs written (which ones a role
 // uses is fixed by EPI; unused pointers are ignored).
 struct EpiPtr {
     const char* i0;
@@ -164,50 +117,6 @@ struct EpiPtr {
     char* o1;
     char* o2;
 };
-
-template <int EPI>
-__device__ __forceinline__ void epi_load(const EpiPtr& a, EpiIn<EPI>& in) {
-    if constexpr (EPI == EPI_RESID) {
-        in.x = *reinterpret_cast<const uint2*>(a.i0);
-    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-        in.g = *reinterpret_cast<const uint2*>(a.i0);
-        in.u = *reinterpret_cast<const uint2*>(a.i1);
-    } else if constexpr (EPI == EPI_ACC_F32) {
-        in.c = *reinterpret_cast<const float4*>(a.i0);
-    }
-}
-
-template <int EPI>
-__device__ __forceinline__ void epi4(const EpiPtr& a, const float (&w)[4], const EpiIn<EPI>& in) {
-    if constexpr (EPI == EPI_STORE_F32) {
-        *reinterpret_cast<float4*>(a.o0) = make_float4(w[0], w[1], w[2], w[3]);
-    } else if constexpr (EPI == EPI_STORE) {
-        *reinterpret_cast<uint2*>(a.o0) = pack4(w);
-    } else if constexpr (EPI == EPI_RESID) {
-        float x[4], y[4];
-        unpack4(in.x, x);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) y[k] = x[k] + w[k];
-        *reinterpret_cast<uint2*>(a.o0) = pack4(y);
-    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-        float g[4], u[4], dg[4], du[4];
-        unpack4(in.g, g);
-        unpack4(in.u, u);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) swiglu_bwd_f(w[k], g[k], u[k], dg[k], du[k]);
-        *reinterpret_cast<uint2*>(a.o0) = pack4(dg);
-        *reinterpret_cast<uint2*>(a.o1) = pack4(du);
-        if (a.o2) {   // optional h = silu(g) u, as the forward computed it
-            float hh[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) hh[k] = swiglu_f(g[k], u[k]);
-            *reinterpret_cast<uint2*>(a.o2) = pack4(hh);
-        }
-    } else if constexpr (EPI == EPI_ACC_F32) {
-        const float4 c = in.c;
-        *reinterpret_cast<float4*>(a.o0) = make_float4(c.x + w[0], c.y + w[1], c.z + w[2], c.w + w[3]);
-    }
-}
 
 // Gate/up pair for hidden columns col..col+3: stores g, u (bf16) and
 // h = silu(g) u computed from the stored values.
@@ -294,16 +203,6 @@ __device__ __forceinline__ void epi8(const EpiPtr& a, const float (&w)[8], const
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
-}
-
-// Direct-to-LDS load of 16 bytes per lane (to LDS address lds + 16 * lane)
-// issued from inline assembly: for the builtin form the compiler makes every
-// later transposing LDS read wait for all loads in flight (it cannot tell
-// that they touch other slots).  The explicit vmcnt waits of the K loop order
-// these loads.  Kernels that use it set M0 nowhere else.
-__device__ __forceinline__ void lds_load16(rsrc_t r, uint32_t lds, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
 }
 
 // MFMA x (0..63) of a K half in growing squares over the 8 x 8 tiles, so the
@@ -608,257 +507,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     else run(std::false_type{});
 }
 
-// ---- M/N-contiguous kernel (weight gradients) -------------------------------
-// 512 threads = 8 wavefronts in a 2 x 4 grid, 128 x 64 per wavefront = 4 x 2
-// tiles of v_mfma_f32_32x32x16_bf16.  A tiles are requested two K steps
-// ahead into three 32 KB slots, B tiles one step ahead into two; one barrier
-// per K step.  An operand tile is 64 k-rows x 256 values, 512 B per k-row,
-// 16-byte chunk c of k-row k at position c ^ 4 (k & 3); each load moves two
-// k-rows, and a 32x32x16 fragment (lane l: column l % 32, k = 8 (l / 32) ..
-// +7) comes from two ds_read_b64_tr_b16.  The transposing read's lane layout,
-// probed on the GPU: within each group of 16 lanes, lane j receives element
-// (j & 3) of the 8-byte blocks addressed by lanes 4e + (j >> 2), e = 0..3.
-template <int EPI>
-__global__ __launch_bounds__(MN_THREADS, 1) void gemm_mn_kernel(const Params p) {
-    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
-    constexpr int ASLOTS = 3;              // A slots; B has two after them
-    constexpr int BBASE = ASLOTS * OPB;
-
-    int tm, tn;
-    tile_coords(p, tm, tn);
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave >> 2, wn = wave & 3;
-    const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * BN;   // first output column
-    const int64_t nb0 = n0;                // first B row
-
-    // Loader: per K step each wavefront moves 4 A and 4 B pieces of 1 KB;
-    // piece q holds k-rows kq[q] = (wave*4+q)*2 + l/32, lane l the LDS chunk
-    // l&31 = logical chunk (l&31) ^ 4*(kq[q]&3); the K step (64 k-rows) rides
-    // in soffset.
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    int kq[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) kq[q] = (wave * 4 + q) * 2 + (lane >> 5);
-    auto mn_off = [&](int q, int64_t col0, int64_t ncols, int64_t ld) -> uint32_t {
-        const int64_t col = col0 + (((lane & 31) ^ (4 * (kq[q] & 3))) * 8);
-        return col < ncols ? (uint32_t)((kq[q] * ld + col) * 2) : OOB;
-    };
-    uint32_t aoff[4], boff[4];
-    uint32_t astep = 0, bstep = 0;   // bytes per K step
-    rsrc_t ar, br;
-    int64_t K = 0;
-    int nk = 0;
-    auto set_seg = [&](int s) {
-        const Seg g = s == 0 ? p.seg[0] : p.seg[1];
-        ar = make_rsrc(g.A, g.a_bytes);
-        br = make_rsrc(g.B, g.b_bytes);
-        K = g.K;
-        nk = (int)((K + BK - 1) / BK);
-        astep = (uint32_t)(BK * g.lda * 2);
-        bstep = (uint32_t)(BK * g.ldb * 2);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            aoff[q] = mn_off(q, m0, p.M, g.lda);
-            boff[q] = mn_off(q, nb0, p.NB, g.ldb);
-        }
-    };
-    // k-rows past the segment's K read zeros; so do tiles past K, with
-    // soffset 0 so that OOB + soffset cannot wrap into the extent
-    auto kin = [&](int kt, int q) { return kq[q] < (int)(K - (int64_t)kt * BK); };
-    const uint32_t lds0 = (uint32_t)(size_t)(LDS_AS char*)smem;
-    auto issueA = [&](int kt, int q) {
-        const int so = (kt % ASLOTS) * OPB + (wave_s * 4 + q) * 1024;
-        const uint32_t ao = kin(kt, q) ? aoff[q] : OOB;
-        lds_load16(ar, lds0 + so, ao, kt < nk ? (uint32_t)kt * astep : 0u);
-    };
-    auto issueB = [&](int kt, int q) {
-        const int so = BBASE + (kt & 1) * OPB + (wave_s * 4 + q) * 1024;
-        const uint32_t bo = kin(kt, q) ? boff[q] : OOB;
-        lds_load16(br, lds0 + so, bo, kt < nk ? (uint32_t)kt * bstep : 0u);
-    };
-
-    // MN fragment of the 32 columns at cb, k = 16*kk .. +15: in 16-lane group
-    // g = l/16, lane s = l%16 addresses k-row 16*kk + 8*(g>>1) + s/4 (+4 for
-    // the second read) at columns cb + 16*(g&1) + 4*(s&3) .. +3, and lane j of
-    // the group receives column cb + 16*(g&1) + j of four consecutive k-rows,
-    // which is the MFMA layout (lane l: column l%32, k = 8*(l/32) .. +7).  The
-    // k-row's low two bits are s/4 for every kk, so the swizzle, and with it
-    // the whole per-lane offset, is fixed.
-    const int tg = lane >> 4, ts = lane & 15;
-    auto mn_lane_off = [&](int cb) -> int {
-        const int ch = ((cb >> 3) + 2 * (tg & 1) + ((ts & 3) >> 1)) ^ (4 * (ts >> 2));
-        return (8 * (tg >> 1) + (ts >> 2)) * 512 + (ch << 4) + ((ts & 1) << 3);
-    };
-    int mn_aoff[4], mn_boff[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mn_aoff[i] = mn_lane_off(wm * 128 + i * 32);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) mn_boff[j] = mn_lane_off(wn * 64 + j * 32);
-    auto mn_frag = [&](uint32_t base, int loff, int kk) -> bf16x8 {
-        LDS_AS char* q = (LDS_AS char*)(size_t)(base + (uint32_t)loff);
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(q + kk * 8192));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(q + kk * 8192 + 2048));
-        const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        return __builtin_bit_cast(bf16x8, v);
-    };
-    auto frags = [&](int kt, int kk, bf16x8 (&a)[4], bf16x8 (&b)[2]) {
-        // slot bases as scalars, so the per-read offsets stay immediates
-        const uint32_t ua = __builtin_amdgcn_readfirstlane(lds0 + (kt % ASLOTS) * OPB);
-        const uint32_t ub = __builtin_amdgcn_readfirstlane(lds0 + BBASE + (kt & 1) * OPB);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = mn_frag(ua, mn_aoff[i], kk);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) b[j] = mn_frag(ub, mn_boff[j], kk);
-    };
-
-    f32x16 acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    // One K step: multiply tile kt while tile kt+1's B (sub-steps 0, 1: its
-    // slot was last read before the previous barrier) and tile kt+2's A
-    // (sub-steps 2, 3) are requested; the barrier waits for all but the last
-    // four requests (tile kt+2's A).
-    auto step = [&](int kt) {
-        bf16x8 fa[2][4], fb[2][2];
-        frags(kt, 0, fa[0], fb[0]);
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            if (kk < 2) { issueB(kt + 1, 2 * kk); issueB(kt + 1, 2 * kk + 1); }
-            else { issueA(kt + 2, 2 * (kk - 2)); issueA(kt + 2, 2 * (kk - 2) + 1); }
-            if (kk + 1 < BK / 16) frags(kt, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-            // keep the next sub-step's fragment reads ahead of this sub-step's
-            // MFMAs (left alone, the scheduler sinks them to their use)
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
-        }
-        // vmcnt(4): all but tile kt+2's four A requests have landed, i.e. tile
-        // kt+1; lgkmcnt(0): this step's fragment reads are done.  A bare
-        // barrier: a fence would also wait for tile kt+2.
-        wait_vm_lgkm0<4>();
-        __builtin_amdgcn_s_barrier();
-    };
-
-    for (int s = 0; s < p.nseg; ++s) {
-        set_seg(s);
-        if (nk == 0) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) { issueA(0, q); issueB(0, q); }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) issueA(1, q);
-        wait_vm_lgkm0<4>();   // tile 0 in LDS
-        __builtin_amdgcn_s_barrier();
-        for (int kt = 0; kt < nk; ++kt) step(kt);
-        // the last steps requested all-zero tiles past K: let them land
-        // before another segment reuses the slots (and before the epilogue)
-        wait_vm_lgkm0<0>();
-        __builtin_amdgcn_s_barrier();
-    }
-    // Epilogue on quad-transposed accumulators: this lane owns tile row
-    // lr + i*32 + q*8 and tile columns lc + j*32 .. +3 of each 32x32 tile.
-    const int jq = lane & 3;
-    const int cq = (lane & 31) & ~3;
-    const int lr = wm * 128 + (lane >> 5) * 4 + jq;
-    const int lc = wn * 64 + cq;
-    const EpiArgs e = p.e;
-    static_assert(EPI == EPI_STORE_F32 || EPI == EPI_ACC_F32, "fp32 epilogues only");
-    constexpr int ESO = 4;                            // output element bytes
-    constexpr bool HAS_IN = EPI == EPI_ACC_F32;
-    constexpr int PD = 1;                             // row groups loaded ahead
-    EpiIn<EPI> in[PD + 1][4][2];
-
-    // Whole tile inside M x N (and, for the split fp32 accumulate, on one side
-    // of nsplit): every operand is a uniform per-tile base plus this lane's
-    // fixed 32-bit offset plus a uniform per-(i, q, j) offset, so the accesses
-    // need no bounds checks and no per-element 64-bit index arithmetic.
-    bool fast = m0 + BM <= p.M && n0 + BN <= p.N;
-    char* ob = nullptr;            // output tile base
-    int64_t old = e.ld0;           // its leading dimension (elements)
-    if constexpr (EPI == EPI_ACC_F32) {
-        if (n0 + BN <= e.nsplit) {
-            ob = static_cast<char*>(e.out0) + (m0 * e.ld0 + n0) * 4;
-        } else if (n0 >= e.nsplit) {
-            ob = static_cast<char*>(e.out1) + (m0 * e.ld1 + (n0 - e.nsplit)) * 4;
-            old = e.ld1;
-        } else {
-            fast = false;
-        }
-    } else {
-        ob = static_cast<char*>(e.out0) + (m0 * e.ld0 + n0) * ESO;
-    }
-    const uint32_t lo = (uint32_t)(((int64_t)lr * old + lc) * ESO);
-    auto fptr = [&](int i, int q, int j) -> EpiPtr {
-        const int64_t uo = ((int64_t)(i * 32 + q * 8) * old + j * 32) * ESO;
-        EpiPtr a{};
-        char* o = ob + uo + lo;
-        a.o0 = o;
-        if constexpr (EPI == EPI_ACC_F32) a.i0 = o;
-        return a;
-    };
-    auto sptr = [&](int64_t row, int64_t col) -> EpiPtr {
-        EpiPtr a{};
-        if constexpr (EPI == EPI_ACC_F32) {
-            float* c = acc_ptr(e, row, col);
-            a.o0 = reinterpret_cast<char*>(c);
-            a.i0 = reinterpret_cast<const char*>(c);
-        } else {
-            a.o0 = static_cast<char*>(e.out0) + (row * e.ld0 + col) * ESO;
-        }
-        return a;
-    };
-
-    auto run = [&](auto fast_c) {
-        constexpr bool FAST = decltype(fast_c)::value;
-        auto ptr = [&](int i, int q, int j) -> EpiPtr {
-            if constexpr (FAST) return fptr(i, q, j);
-            else return sptr(m0 + lr + i * 32 + q * 8, n0 + lc + j * 32);
-        };
-        auto ok = [&](int i, int q, int j) -> bool {
-            if constexpr (FAST) return true;
-            else return m0 + lr + i * 32 + q * 8 < p.M && n0 + lc + j * 32 < p.N;
-        };
-        auto prefetch = [&](int i, EpiIn<EPI> (&dst)[4][2]) {
-            if constexpr (HAS_IN) {
-#pragma clang loop unroll(full)
-                for (int q = 0; q < 4; ++q)
-#pragma clang loop unroll(full)
-                    for (int j = 0; j < 2; ++j)
-                        if (ok(i, q, j)) epi_load<EPI>(ptr(i, q, j), dst[q][j]);
-            }
-        };
-#pragma clang loop unroll(full)
-        for (int i = 0; i < PD; ++i) prefetch(i, in[i]);
-#pragma clang loop unroll(full)
-        for (int i = 0; i < 4; ++i) {
-            if (i + PD < 4) prefetch(i + PD, in[(i + PD) % (PD + 1)]);
-#pragma clang loop unroll(full)
-            for (int q = 0; q < 4; ++q) {
-                float w[2][4];
-#pragma clang loop unroll(full)
-                for (int j = 0; j < 2; ++j) {
-                    const float v[4] = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
-                    quad_transpose(v, w[j], (jq & 1) != 0, (jq & 2) != 0);
-                }
-#pragma clang loop unroll(full)
-                for (int j = 0; j < 2; ++j)
-                    if (ok(i, q, j)) epi4<EPI>(ptr(i, q, j), w[j], in[i % (PD + 1)][q][j]);
-            }
-        }
-    };
-    if (fast) run(std::true_type{});
-    else run(std::false_type{});
-}
-
-
 // Byte extent of a row-major operand: (rows-1)*ld + cols elements of bf16.
 inline bool extent(int64_t rows, int64_t ld, int64_t cols, uint32_t& out) {
     const int64_t b = rows <= 0 ? 0 : ((rows - 1) * ld + cols) * 2;
@@ -873,37 +521,28 @@ hipError_t launch(const Params& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int EPI>
-hipError_t launch_mn(const Params& p, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_mn_kernel<EPI>), dim3(p.tiles_m * p.tiles_n), dim3(MN_THREADS), 0, s, p);
-    return hipGetLastError();
-}
-
 }  // namespace
 
 int64_t swiglu_b_rows(int64_t ffn) { return 2 * ((ffn + 31) / 32) * 32; }
 
-// Requires A and B both K-contiguous, or both M/N-contiguous (then only with
-// the fp32 store or accumulate epilogue), 16-byte aligned rows, every operand
-// extent under 2 GB.  With the SwiGLU map, B is the gate/up weight
-// interleaved per 32 hidden columns (32 gate rows, then 32 up rows;
-// swiglu_b_rows(N) rows) and N is the number of hidden columns.
+// Requires A and B K-contiguous, every operand extent under 2 GB, N, the
+// output and input leading dimensions and the SwiGLU-backward split column
+// multiples of 8 and the epilogue pointers 16-byte aligned (the epilogue
+// moves 8 consecutive output columns, SwiGLU 4 hidden columns, per 16-byte
+// access); the fp32 accumulate writes out0 only (nsplit >= N).  With the
+// SwiGLU map, B is the gate/up weight interleaved per 32 hidden columns (32
+// gate rows, then 32 up rows; swiglu_b_rows(N) rows) and N is the number of
+// hidden columns.
 hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
-    const bool mn = !a.a_kcontig;
-    if (a.b_kcontig == mn) return hipErrorInvalidValue;
-    if (mn && (a.swiglu_map || (a.epi != EPI_STORE_F32 && a.epi != EPI_ACC_F32))) return hipErrorInvalidValue;
-    // the K-contiguous epilogue moves 8 consecutive output columns (SwiGLU: 4
-    // hidden columns) with 16-byte accesses
-    if (!mn) {
-        const bool in = a.epi == EPI_RESID || a.epi == EPI_SWIGLU_BWD;
-        if (a.N % 8 || a.e.ld0 % 8 || (in && a.e.ldi0 % 8) || (a.epi == EPI_SWIGLU_BWD && a.e.nsplit % 8))
-            return hipErrorInvalidValue;
-        if (a.epi == EPI_ACC_F32 && a.e.nsplit < a.N) return hipErrorInvalidValue;   // out0 only
-        const uintptr_t ptrs = reinterpret_cast<uintptr_t>(a.e.out0) | reinterpret_cast<uintptr_t>(a.e.out1) |
-                               reinterpret_cast<uintptr_t>(a.e.out2) | reinterpret_cast<uintptr_t>(a.e.in0) |
-                               reinterpret_cast<uintptr_t>(a.e.in1);
-        if (ptrs % 16) return hipErrorInvalidValue;
-    }
+    if (!a.a_kcontig || !a.b_kcontig) return hipErrorInvalidValue;
+    const bool in = a.epi == EPI_RESID || a.epi == EPI_SWIGLU_BWD;
+    if (a.N % 8 || a.e.ld0 % 8 || (in && a.e.ldi0 % 8) || (a.epi == EPI_SWIGLU_BWD && a.e.nsplit % 8))
+        return hipErrorInvalidValue;
+    if (a.epi == EPI_ACC_F32 && a.e.nsplit < a.N) return hipErrorInvalidValue;
+    const uintptr_t ptrs = reinterpret_cast<uintptr_t>(a.e.out0) | reinterpret_cast<uintptr_t>(a.e.out1) |
+                           reinterpret_cast<uintptr_t>(a.e.out2) | reinterpret_cast<uintptr_t>(a.e.in0) |
+                           reinterpret_cast<uintptr_t>(a.e.in1);
+    if (ptrs % 16) return hipErrorInvalidValue;
     Params p{};
     p.M = a.M;
     p.N = a.N;
@@ -920,15 +559,11 @@ hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
         p.seg[i].lda = g.lda;
         p.seg[i].ldb = g.ldb;
         p.seg[i].K = g.K;
-        if (mn && (g.lda % 8 || g.ldb % 8 || (reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B)) % 16))
-            return hipErrorInvalidValue;
-        const bool ok = mn ? extent(g.K, g.lda, a.M, p.seg[i].a_bytes) && extent(g.K, g.ldb, p.NB, p.seg[i].b_bytes)
-                           : extent(a.M, g.lda, g.K, p.seg[i].a_bytes) && extent(p.NB, g.ldb, g.K, p.seg[i].b_bytes);
+        const bool ok = extent(a.M, g.lda, g.K, p.seg[i].a_bytes) && extent(p.NB, g.ldb, g.K, p.seg[i].b_bytes);
         if (!ok) return hipErrorInvalidValue;
     }
     p.e = a.e;
     if (p.tiles_m == 0 || p.tiles_n == 0) return hipSuccess;
-    if (mn) return a.epi == EPI_ACC_F32 ? launch_mn<EPI_ACC_F32>(p, s) : launch_mn<EPI_STORE_F32>(p, s);
     switch (a.epi) {
         case EPI_SWIGLU: return launch<EPI_SWIGLU>(p, s);
         case EPI_RESID: return launch<EPI_RESID>(p, s);

@@ -22,7 +22,7 @@ enum Epi {
     EPI_SWIGLU_BWD = 3,  // dh=acc; g=in0,u=in1 (ldi0) -> out0[m*ld0+n]=dg, out0[..+nsplit]=du,
                          // and if out2: out2[m*ldi0+n] = h = silu(g) u
     EPI_ACC_F32 = 4,     // n <  nsplit: out0[m*ld0+n] += acc; else out1[m*ld1+n-nsplit] += acc
-                         // (bf16 K-contiguous operands: out0 only, nsplit >= N)
+                         // (bf16: out0 only, nsplit >= N)
     EPI_BIAS_GELU = 5,   // z = acc + bias[n]; out0 = z, out1 = GELU(z)   (fp32 only)
     EPI_STORE = 6,       // out0[m*ld0+n] = acc                           (storage type)
 };
@@ -50,8 +50,7 @@ struct GemmArgs {
     int64_t M = 0, N = 0;       // output rows / columns (SwiGLU map: N = ffn)
     int nseg = 1;
     GemmSeg seg[2];
-    // bf16: both K-contiguous, or both M/N-contiguous (fp32 epilogues only);
-    // fp32: any combination.
+    // bf16: both K-contiguous; fp32: any combination.
     bool a_kcontig = true;
     bool b_kcontig = false;
     bool swiglu_map = false;    // B columns: per 2*H group, H from B then H from B2

@@ -191,11 +191,12 @@ int validate_desc(const pps_stage_desc* d) {
     if (!(d->eps >= 0.0f)) return PPS_EINVAL;
     if (d->block_type == PPS_BLOCK_SWIGLU && d->dtype == PPS_DTYPE_BF16) {
         // The MFMA GEMM addresses each operand with 32-bit byte offsets: the
-        // largest ones (dg|du [T, 2 ffn], the interleaved gate/up weight copy)
+        // largest ones (dg|du [T, 2 ffn] and its T-contiguous copy, rows
+        // padded to a multiple of 8; the interleaved gate/up weight copy)
         // must stay under 2 GiB.
-        const double lim = 2147483648.0, T = (double)d->T;
+        const double lim = 2147483648.0, Tp = (double)((d->T + 7) / 8 * 8);
         const double f2 = 2.0 * (double)d->ffn, rows = (double)pps::swiglu_b_rows(d->ffn);
-        if (T * f2 * 2 >= lim || rows * (double)d->d * 2 >= lim) return PPS_EINVAL;
+        if (Tp * f2 * 2 >= lim || rows * (double)d->d * 2 >= lim) return PPS_EINVAL;
     }
     if ((d->flags & PPS_FLAG_PROFILE) && d->profile_capacity < 0) return PPS_EINVAL;
     if (!(d->flags & PPS_FLAG_BOOKKEEPING_ONLY)) {
