@@ -36,10 +36,10 @@ PEAK_HBM_GBS = 8000.0
 # copy kernel measured in the same runs).  Valid only for the GEMM source they were taken on.
 TRAFFIC = {
     "config": "c3_80layer_p8_stage0",
-    "gemm_source_sha1": "f1d459bac5b4dfa9a5d41dc8228b3311a6e03d65",
+    "gemm_source_sha1": "85c199bcd48b2dc210598ec386bee64d38d871b3",
     "bytes_per_launch": {
-        "gemm_gateup_swiglu": 13.59e9, "gemm_down_residual": 6.002e9, "gemm_dh_swiglu_bwd": 8.802e9,
-        "gemm_dn": 12.86e9, "gemm_wgrad_down": 8.452e9, "gemm_wgrad_gateup": 8.452e9,
+        "gemm_gateup_swiglu": 13.37e9, "gemm_down_residual": 5.98e9, "gemm_dh_swiglu_bwd": 8.84e9,
+        "gemm_dn": 12.27e9, "gemm_wgrad_down": 8.291e9, "gemm_wgrad_gateup": 8.291e9,
     },
 }
 

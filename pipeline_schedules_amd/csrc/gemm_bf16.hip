@@ -178,25 +178,27 @@ __device__ __forceinline__ void epi8(const EpiPtr& a, const float (&w)[8], const
 #pragma unroll
         for (int k = 0; k < 8; ++k) y[k] = x[k] + w[k];
         *reinterpret_cast<uint4*>(a.o0) = pack8(y);
-    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-        float g[8], u[8], dg[8], du[8];
-        unpack8(in.g, g);
-        unpack8(in.u, u);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) swiglu_bwd_f(w[k], g[k], u[k], dg[k], du[k]);
-        *reinterpret_cast<uint4*>(a.o0) = pack8(dg);
-        *reinterpret_cast<uint4*>(a.o1) = pack8(du);
-        if (a.o2) {   // optional h = silu(g) u, as the forward computed it
-            float hh[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) hh[k] = swiglu_f(g[k], u[k]);
-            *reinterpret_cast<uint4*>(a.o2) = pack8(hh);
-        }
     } else if constexpr (EPI == EPI_ACC_F32) {
         const float4 c0 = in.c0, c1 = in.c1;
         reinterpret_cast<float4*>(a.o0)[0] = make_float4(c0.x + w[0], c0.y + w[1], c0.z + w[2], c0.w + w[3]);
         reinterpret_cast<float4*>(a.o0)[1] = make_float4(c1.x + w[4], c1.y + w[5], c1.z + w[6], c1.w + w[7]);
     }
+}
+
+// SwiGLU backward for 8 columns: stores dg, du and returns h = silu(g) u (as
+// the forward computed it) for the caller to store transposed.
+__device__ __forceinline__ void epi8_swiglu_bwd(const EpiPtr& a, const float (&w)[8], const EpiIn8<EPI_SWIGLU_BWD>& in,
+                                                float (&hh)[8]) {
+    float g[8], u[8], dg[8], du[8];
+    unpack8(in.g, g);
+    unpack8(in.u, u);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        swiglu_bwd_f(w[k], g[k], u[k], dg[k], du[k]);
+        hh[k] = swiglu_f(g[k], u[k]);
+    }
+    *reinterpret_cast<uint4*>(a.o0) = pack8(dg);
+    *reinterpret_cast<uint4*>(a.o1) = pack8(du);
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt left at its maximum).
@@ -434,7 +436,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
             const int64_t ui = ((int64_t)(i * 16 + r) * e.ldi0 + m0 * e.ldi0 + n0) * 2;
             a.i0 = static_cast<const char*>(e.in0) + ui + li;
             a.i1 = static_cast<const char*>(e.in1) + ui + li;
-            a.o2 = e.out2 ? static_cast<char*>(e.out2) + ui + li : nullptr;
         } else if constexpr (EPI == EPI_RESID) {
             a.i0 = static_cast<const char*>(e.in0) + ((int64_t)(i * 16 + r) * e.ldi0 + m0 * e.ldi0 + n0) * 2 + li;
         } else if constexpr (EPI == EPI_ACC_F32) {
@@ -457,7 +458,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
                 a.o1 = a.o0 + e.nsplit * 2;
                 a.i0 = static_cast<const char*>(e.in0) + (row * e.ldi0 + col) * 2;
                 a.i1 = static_cast<const char*>(e.in1) + (row * e.ldi0 + col) * 2;
-                a.o2 = e.out2 ? static_cast<char*>(e.out2) + (row * e.ldi0 + col) * 2 : nullptr;
             } else if constexpr (EPI == EPI_RESID) {
                 a.i0 = static_cast<const char*>(e.in0) + (row * e.ldi0 + col) * 2;
             }
@@ -488,9 +488,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             if (i + 1 < 8) prefetch(i + 1, in[(i + 1) & 1]);
+            float hh[4][8];   // SwiGLU backward: h of this row group
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                if constexpr (EPI == EPI_SWIGLU) {
+                if constexpr (EPI == EPI_SWIGLU_BWD) {
+                    float w[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) w[j] = acc[i][j][r];
+                    if (ok(i, r)) epi8_swiglu_bwd(ptr(i, r), w, in[i & 1][r], hh[r]);
+                } else if constexpr (EPI == EPI_SWIGLU) {
                     const float g[4] = {acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
                     const float u[4] = {acc[i][4][r], acc[i][5][r], acc[i][6][r], acc[i][7][r]};
                     if (ok(i, r)) epi4_swiglu(ptr(i, r), g, u);
@@ -499,6 +505,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j) w[j] = acc[i][j][r];
                     if (ok(i, r)) epi8<EPI>(ptr(i, r), w, in[i & 1][r]);
+                }
+            }
+            if constexpr (EPI == EPI_SWIGLU_BWD && FAST) {
+                // h = silu(g) u (as the forward computed it) for the weight
+                // gradient, written transposed: column j's four rows of this
+                // row group are 8 consecutive bytes of hT row n0 + lc + j
+                // (only full tiles: the dispatcher requires them with out2)
+                if (e.out2) {
+                    const int64_t row0 = m0 + lr + i * 16;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int64_t col = n0 + lc + j;
+                        const float v[4] = {hh[0][j], hh[1][j], hh[2][j], hh[3][j]};
+                        uint2* o = reinterpret_cast<uint2*>(static_cast<char*>(e.out2) + (col * e.ld2 + row0) * 2);
+                        *o = pack4(v);
+                    }
                 }
             }
         }
@@ -539,6 +561,8 @@ hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
     if (a.N % 8 || a.e.ld0 % 8 || (in && a.e.ldi0 % 8) || (a.epi == EPI_SWIGLU_BWD && a.e.nsplit % 8))
         return hipErrorInvalidValue;
     if (a.epi == EPI_ACC_F32 && a.e.nsplit < a.N) return hipErrorInvalidValue;
+    if (a.epi == EPI_SWIGLU_BWD && a.e.out2 && (a.M % BM || a.N % BN || a.e.ld2 < a.M || a.e.ld2 % 4))
+        return hipErrorInvalidValue;   // h is written transposed from full tiles only
     const uintptr_t ptrs = reinterpret_cast<uintptr_t>(a.e.out0) | reinterpret_cast<uintptr_t>(a.e.out1) |
                            reinterpret_cast<uintptr_t>(a.e.out2) | reinterpret_cast<uintptr_t>(a.e.in0) |
                            reinterpret_cast<uintptr_t>(a.e.in1);

@@ -20,7 +20,8 @@ enum Epi {
     EPI_RESID = 1,       // out0[m*ld0+n] = in0[m*ldi0+n] + acc           (storage type)
     EPI_SWIGLU = 2,      // g,u pair -> out0=g, out1=u, out2=h=silu(g)*u  (storage type, ld0)
     EPI_SWIGLU_BWD = 3,  // dh=acc; g=in0,u=in1 (ldi0) -> out0[m*ld0+n]=dg, out0[..+nsplit]=du,
-                         // and if out2: out2[m*ldi0+n] = h = silu(g) u
+                         // and if out2: h = silu(g) u at out2[m*ldi0+n] (fp32 GEMM) or
+                         // out2[n*ld2+m] (bf16 GEMM)
     EPI_ACC_F32 = 4,     // n <  nsplit: out0[m*ld0+n] += acc; else out1[m*ld1+n-nsplit] += acc
                          // (bf16: out0 only, nsplit >= N)
     EPI_BIAS_GELU = 5,   // z = acc + bias[n]; out0 = z, out1 = GELU(z)   (fp32 only)
@@ -37,6 +38,8 @@ struct EpiArgs {
     int64_t ldi0 = 0;
     int64_t nsplit = 0;
     const float* bias = nullptr;
+    int64_t ld2 = 0;   // SwiGLU backward, bf16 GEMM: h is written transposed, out2[n*ld2 + m]
+                       // (needs M and N multiples of 256, ld2 % 4 == 0)
 };
 
 struct GemmSeg {

@@ -329,8 +329,13 @@ int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_
 // Weight gradient of block b: dWd += h^T dy; dWg += n^T dg; dWu += n^T du.
 // The GEMMs reduce over the T rows.  bf16: the operands are first copied
 // T-contiguous ([features, T]) for the K-contiguous kernel; fp32 reads them as
-// stored.  n and h are in the scratch buffers when `have_nh` (the backward
-// just produced them); otherwise they are recomputed from the stash.
+// stored.  With `have_nh` the backward just produced n (scratch) and h
+// (bf16: already T-contiguous, written so by the dh epilogue; fp32: scratch);
+// otherwise both are recomputed from the stash.
+// bf16 without the split: the dh epilogue writes hT (T and ffn multiples of
+// the 256 x 256 GEMM tile)
+bool hT_fused(const pps_stage* h) { return h->tn && h->d.T % 256 == 0 && h->d.ffn % 256 == 0; }
+
 int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, const void* dgu, bool have_nh) {
     const pps_stage_desc& D = h->d;
     const int64_t T = D.T, d = D.d, f = D.ffn;
@@ -369,7 +374,7 @@ int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, cons
                 return pps::transpose_bf16(src, T, cols, cols, dst, Tp, 0, 0, h->stream);
             });
         };
-        PPS_TRY(tr(sh, f, hT));
+        if (!have_nh) PPS_TRY(tr(sh, f, hT));
         PPS_TRY(tr(dy, d, dyT));
         PPS_TRY(tr(sn, d, nT));
         PPS_TRY(tr(dgu, 2 * f, dguT));
@@ -444,6 +449,12 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
         a.epi = pps::EPI_SWIGLU_BWD;
         a.e.in0 = ab + h->lay.g[b]; a.e.in1 = ab + h->lay.u[b]; a.e.ldi0 = f;
         a.e.out0 = dgu; a.e.ld0 = 2 * f; a.e.nsplit = f; a.e.out2 = sh;
+        if (h->tn && sh) {
+            // the weight gradient reads h T-contiguous: the epilogue writes it
+            // so when its tiles are full; otherwise h and n are recomputed at dW
+            a.e.out2 = hT_fused(h) ? h->scratch + h->s_hT : nullptr;
+            a.e.ld2 = h->Tp;
+        }
         PPS_TRY(timed(h, PPS_K_DH, gemm_flops(T, f, d), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
         // dn = dg Wg^T + du Wu^T (one accumulator, K = 2 ffn).
         GemmArgs c;
@@ -468,7 +479,7 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
             return pps::column_reduce_acc(part, T > 0 ? prow : 0, d, dgam, h->stream);
         }));
         if (!h->split) {
-            int rc = swiglu_weight(h, slot, chunk, b, dy, dgu, true);
+            int rc = swiglu_weight(h, slot, chunk, b, dy, dgu, !h->tn || hT_fused(h));
             if (rc != PPS_OK) return rc;
         }
     }
@@ -676,6 +687,11 @@ extern "C" int pps_stage_create(const pps_stage_desc* desc, pps_stage** out) {
             return PPS_ENOMEM;
         }
         if (pps::fill_zero(h->grads, (int64_t)h->grad_bytes, h->stream) != hipSuccess) { release(h); return PPS_EHIP; }
+        // hT's padding columns [T, Tp) are read by the K tail of dW_d and never written
+        if (h->tn && pps::fill_zero(h->scratch + h->s_hT, (int64_t)desc->ffn * h->Tp * 2, h->stream) != hipSuccess) {
+            release(h);
+            return PPS_EHIP;
+        }
         // the padding rows of the interleaved gate/up copy must read as zero
         if (h->wcopy && pps::fill_zero(h->wcopy, (int64_t)h->wcopy_bytes, h->stream) != hipSuccess) { release(h); return PPS_EHIP; }
         if (h->profile) {
