@@ -253,11 +253,11 @@ int pps_stage_get_oplog(const pps_stage* h, pps_op* ops, int cap, int* n);
 #define PPS_K_RMSNORM_FWD   0  /* r = rsqrt(mean x^2 + eps); n = x r gamma      */
 #define PPS_K_GATEUP        1  /* g,u = n [Wg|Wu]; h = silu(g) u                */
 #define PPS_K_DOWN          2  /* y = x + h Wd                                  */
-#define PPS_K_DH            3  /* dh = dy Wd^T; dg, du (SwiGLU backward); h     */
+#define PPS_K_DH            3  /* dh = dy Wd^T; dg, du (SwiGLU backward); h (bf16: h^T) */
 #define PPS_K_DN            4  /* dn = dg Wg^T + du Wu^T                         */
 #define PPS_K_RMSNORM_BWD   5  /* dx = dy + r a - r^3 x (a.x)/d; dgamma partials; n */
 #define PPS_K_DGAMMA        6  /* dgamma += sum of partials                      */
-#define PPS_K_PREP_W        7  /* split W: n = x r gamma, h = silu(g) u again    */
+#define PPS_K_PREP_W        7  /* n = x r gamma, h = silu(g) u again at W: split, or bf16 with T or ffn not multiples of 256 */
 #define PPS_K_WGRAD_DOWN    8  /* dWd += h^T dy                                  */
 #define PPS_K_WGRAD_GATEUP  9  /* dWg += n^T dg, dWu += n^T du                   */
 #define PPS_K_COPY         10  /* copies: into the stash; per-pass weight copies; T-contiguous h, n, dy, dg|du for bf16 dW */
