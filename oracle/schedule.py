@@ -21,9 +21,14 @@ Readings of points the pages leave open:
   * interleaved order (v >= 2): Megatron-style groups of P micro-batches per
     chunk, warmup 2(P-k-1) + (v-1)P + 1 forwards; requires M % P == 0
     ([Sched §06] notes divisibility constraints).
-  * ZB1P: keep the 1F1B F/B order; a stage that cannot run its next F/B
-    (dependency not done, or an F that would exceed the activation budget
-    P-k counted until W) runs its oldest pending W ([GPipe->ZB ZB1P 与 ZB2P]).
+  * ZB1P / ZB2P ([GPipe->ZB ZB1P 与 ZB2P]): the page sets the number of
+    micro-batches a stage may hold with their backward unfinished to p (ZB1P)
+    or 2p (ZB2P), p = P the number of stages, the same on every stage.  ZB1P
+    keeps the 1F1B F/B order; ZB2P warms up with more forwards, as many as a
+    stage can run before its first backward can start under equal F/B/W costs
+    (2(P-k)-1), then alternates B and F.  A stage that cannot run its next F/B
+    (dependency not done, or an F that would exceed the budget, counted until
+    W) runs its oldest pending W.
   * stash slot = lowest free index, taken at F, freed at B (or at W when
     the backward is split).
 """
@@ -227,20 +232,55 @@ def simulate(lists, v=1):
     return starts
 
 
-def simulate_zb(P, M, budget_scale=1):
+def zb_warmup(P, M, k, budget_scale):
+    """Forwards before the first backward of stage k under ZB1P/ZB2P.
+
+    ZB1P keeps the 1F1B warmup, P-k.  ZB2P "does more forwards in warmup" so
+    that the later backwards are ready sooner ([GPipe->ZB ZB1P 与 ZB2P]); the
+    reading taken: a stage keeps running forwards until its first backward can
+    start.  With unit costs stage k's first forward starts at t = k and the
+    gradient of micro-batch 0 reaches it at t = 2P-1-k (P-1-k forwards on the
+    way down, P-k backwards on the way back), leaving 2(P-k)-1 slots.
+    """
+    w = P - k if budget_scale == 1 else 2 * (P - k) - 1
+    return min(w, M)
+
+
+def zb_budget(P, budget_scale):
+    """Micro-batches a stage may hold with W not yet done: p for ZB1P, 2p for
+    ZB2P, the same on every stage ([GPipe->ZB ZB1P 与 ZB2P]: for a 4-stage
+    pipeline the two limits are 4 and 8 micro-batches)."""
+    return budget_scale * P
+
+
+def zb_fb_order(P, M, k, budget_scale, warmup=None):
+    """The F/B order of a ZB stage: the warmup forwards, then one B (oldest
+    first) and one F alternating, then the remaining backwards."""
+    w = zb_warmup(P, M, k, budget_scale) if warmup is None else min(warmup, M)
+    ops = [(F, i, 0) for i in range(w)]
+    for j in range(M - w):
+        ops.append((B, j, 0))
+        ops.append((F, w + j, 0))
+    ops += [(B, j, 0) for j in range(M - w, M)]
+    return ops
+
+
+def simulate_zb(P, M, budget_scale=1, warmups=None):
     """Zero-Bubble greedy placement of deferred W ops ([GPipe->ZB ZB1P 与 ZB2P]).
 
-    Each stage keeps its 1F1B F/B order.  At every integer time t a free stage
-    (1) runs its next F/B if that op's dependencies ended at or before t and,
-    for an F, its live count stays below the budget ``budget_scale*(P-k)``;
-    (2) otherwise runs its oldest pending W; (3) otherwise idles.  ``live``
-    counts entries whose F has started and whose W has not yet run.
-    ``budget_scale`` 1 is ZB1P, 2 is the ZB2P budget.
+    Each stage keeps its F/B order (``zb_fb_order``).  At every integer time t
+    a free stage (1) runs its next F/B if that op's dependencies ended at or
+    before t and, for an F, its live count stays below ``zb_budget``; (2)
+    otherwise runs its oldest pending W; (3) otherwise idles.  ``live`` counts
+    entries whose F has started and whose W has not yet run.
+    ``budget_scale`` 1 is ZB1P, 2 is ZB2P.  ``warmups`` (per stage) replaces
+    the warmup counts, for tests that show the ZB2P warmup is tight.
 
     Returns (lists, starts): the per-stage op lists with W ops placed, and
     their start times.
     """
-    base = [one_f_one_b(P, M, k) for k in range(P)]
+    base = [zb_fb_order(P, M, k, budget_scale, None if warmups is None else warmups[k]) for k in range(P)]
+    budget = zb_budget(P, budget_scale)
     ptr = [0] * P
     pending = [deque() for _ in range(P)]
     live = [0] * P
@@ -262,7 +302,7 @@ def simulate_zb(P, M, budget_scale=1):
                 op = base[k][ptr[k]]
                 deps = _deps(op, k, P, 1)
                 ok = all(d in end and end[d] <= t for d in deps)
-                if ok and op[0] == F and live[k] >= budget_scale * (P - k):
+                if ok and op[0] == F and live[k] >= budget:
                     ok = False
                 if ok:
                     ran = op
@@ -283,6 +323,16 @@ def simulate_zb(P, M, budget_scale=1):
                 free_at[k] = t + 1
         t += 1
     return lists, starts
+
+
+def idle_in_span(ops, st):
+    """Idle unit slots between a stage's first op start and its last op end:
+    the compute bubble the Zero-Bubble schedules fill ([GPipe->ZB ZB1P 与
+    ZB2P]; the slots before a stage's first op and after its last are the
+    pipeline's fill and drain)."""
+    if not st:
+        return 0
+    return st[-1] + 1 - st[0] - len(ops)
 
 
 # ---------------------------------------------------------------------------

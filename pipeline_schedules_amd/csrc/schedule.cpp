@@ -24,11 +24,11 @@ namespace {
 
 // ---- closed-form op lists --------------------------------------------------
 
-// [1F1B §2.3/§3.2]: min(P-k, M) warmup forwards, then (B oldest, F next)
-// pairs, then the remaining backwards.
-void list_1f1b(int P, int M, int k, std::vector<Op3>& out) {
+// `warm` forwards, then (B oldest, F next) pairs, then the remaining
+// backwards.
+void list_warm_alternate(int M, int warm, std::vector<Op3>& out) {
     out.clear();
-    const int warm = std::min(P - k, M);
+    warm = std::min(warm, M);
     int next_f = 0, next_b = 0;
     while (next_f < warm) out.push_back({OP_F, next_f++, 0});
     while (next_f < M) {
@@ -37,6 +37,9 @@ void list_1f1b(int P, int M, int k, std::vector<Op3>& out) {
     }
     while (next_b < M) out.push_back({OP_B, next_b++, 0});
 }
+
+// [1F1B §2.3/§3.2]: P-k warmup forwards, then alternate.
+void list_1f1b(int P, int M, int k, std::vector<Op3>& out) { list_warm_alternate(M, P - k, out); }
 
 // [Sched §02]: every forward, then the backwards from the last micro-batch down.
 void list_gpipe(int M, std::vector<Op3>& out) {
@@ -175,15 +178,21 @@ bool run_timed(const std::vector<std::vector<Op3>>& lists, int P, int M, int v, 
     return true;
 }
 
-// Zero-Bubble placement ([GPipe->ZB ZB1P 与 ZB2P]).  Each device keeps its
-// 1F1B F/B order; at each time step a free device runs its next F/B if the
-// dependencies ended by now and (for F) its live count is below the budget;
-// otherwise its oldest pending W; otherwise it idles.  Live = entries whose
-// F has started and whose W has not.
+// Zero-Bubble placement ([GPipe->ZB ZB1P 与 ZB2P]).  The page limits the
+// micro-batches a device holds with their weight gradient not yet done to p
+// (ZB1P) or 2p (ZB2P), p = P, on every device.  ZB1P keeps the 1F1B F/B
+// order; ZB2P warms up with 2(P-k)-1 forwards, the slots device k has before
+// its first backward can start under equal F/B/W costs, then alternates.  At
+// each time step a free device runs its next F/B if the dependencies ended by
+// now and (for F) its live count is below the budget; otherwise its oldest
+// pending W; otherwise it idles.  Live = entries whose F has started and
+// whose W has not.
 bool run_zb(int P, int M, int budget_scale, std::vector<std::vector<Op3>>& lists,
             std::vector<std::vector<int>>& start) {
     std::vector<std::vector<Op3>> base(P);
-    for (int d = 0; d < P; ++d) list_1f1b(P, M, d, base[d]);
+    for (int d = 0; d < P; ++d)
+        list_warm_alternate(M, budget_scale == 1 ? P - d : 2 * (P - d) - 1, base[d]);
+    const int budget = budget_scale * P;
     EndTimes e(P, M, 1);
     std::vector<size_t> pos(P, 0);
     std::vector<std::deque<int>> pend(P);
@@ -204,7 +213,7 @@ bool run_zb(int P, int M, int budget_scale, std::vector<std::vector<Op3>>& lists
                 op = base[d][pos[d]];
                 int r = ready_time(e, op, d);
                 bool ok = r >= 0 && r <= t;
-                if (ok && op.kind == OP_F && live[d] >= budget_scale * (P - d)) ok = false;
+                if (ok && op.kind == OP_F && live[d] >= budget) ok = false;
                 if (ok) {
                     ++pos[d];
                     if (op.kind == OP_F) ++live[d];

@@ -78,6 +78,10 @@ def test_make_schedule_headline_values():
     assert len(ops) == 64 and max(o[4] for o in ops) == 23
     ops = pps.make_schedule(4, 32, 0, 1, pps.ZB1P)
     assert len(ops) == 96 and max(o[4] for o in ops) == 4
+    ops = pps.make_schedule(4, 32, 0, 1, pps.ZB2P)
+    assert len(ops) == 96 and max(o[4] for o in ops) == 8
+    assert [o[0] for o in ops].index(pps.OP_B) == 7            # 2(P-k)-1 warmup forwards
+    assert ops[-1][5] + 1 - ops[0][5] == 96                    # no idle slot in stage 0's span
 
 
 def test_make_schedule_errors():

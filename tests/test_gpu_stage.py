@@ -96,6 +96,27 @@ def test_split_is_bit_identical_to_unsplit(env):
     assert b[3]["peak_live_bytes"] > a[3]["peak_live_bytes"]
 
 
+@pytest.mark.parametrize("kind", ["zb1p", "zb2p"])
+def test_zero_bubble_stage0_extra_warmup(env, kind):
+    # P=4, M=8, stage 0: ZB2P runs 7 forwards before its first backward and
+    # holds up to 8 entries until their W; ZB1P holds 4.  Same kernels in the
+    # same per-micro-batch order as the unsplit 1F1B run, so the results are
+    # bit-identical to it, and within tolerance of the oracle.
+    from pipeline_schedules_amd.inputs import make_inputs
+    cfg = _swiglu_cfg("bf16", T=264, d=264, f=392, L=1, M=8, P=4)
+    inp = make_inputs(cfg, gamma="random")
+    a = _run_single(env, cfg, inp, "1f1b")
+    b = _run_single(env, cfg, inp, kind)
+    _check(cfg, b, inp, TOL["bf16"])
+    assert b[3]["peak_live_entries"] == (8 if kind == "zb2p" else 4)
+    for i in range(cfg.M):
+        assert np.array_equal(a[0][i], b[0][i])
+        assert np.array_equal(a[1][i], b[1][i])
+    for blk in range(cfg.L):
+        for key in a[2][blk]:
+            assert np.array_equal(a[2][blk][key], b[2][blk][key]), key
+
+
 def test_fused_hT_full_tiles(env):
     # T and ffn multiples of the 256 x 256 GEMM tile: the dh epilogue writes
     # h transposed for dW_d (no recompute, no copy).  Parity with the oracle,

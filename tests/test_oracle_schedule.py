@@ -233,19 +233,28 @@ def test_interleaved_needs_divisible_m():
         S.interleaved(4, 6, 0, 2)
 
 
-# --- ZB1P: [GPipe->ZB ZB1P 与 ZB2P] ------------------------------------------
+# --- ZB1P / ZB2P: [GPipe->ZB ZB1P 与 ZB2P] -----------------------------------
 
-def test_zb1p_invariants():
+def _zb_idle(lists, starts):
+    return [S.idle_in_span(o, t) for o, t in zip(lists, starts)]
+
+
+@pytest.mark.parametrize("scale", [1, 2])
+def test_zb_invariants(scale):
     for P in (1, 2, 3, 4, 8):
         for M in (1, P, 2 * P, 8 * P):
-            lists, starts = S.simulate_zb(P, M, 1)
+            lists, starts = S.simulate_zb(P, M, scale)
             for k in range(P):
                 ops = lists[k]
                 kinds = [o[0] for o in ops]
                 assert kinds.count(S.F) == kinds.count(S.B) == kinds.count(S.W) == M
-                # F/B keep the 1F1B order
-                assert [o for o in ops if o[0] != S.W] == S.one_f_one_b(P, M, k)
-                # every W after its own B, oldest first
+                fb = [o for o in ops if o[0] != S.W]
+                # F/B in the stage's ZB order; ZB1P keeps the 1F1B order
+                assert fb == S.zb_fb_order(P, M, k, scale)
+                if scale == 1:
+                    assert fb == S.one_f_one_b(P, M, k)
+                # backwards oldest first; every W after its own B, oldest first
+                assert [o[1] for o in ops if o[0] == S.B] == list(range(M))
                 seen_b = []
                 for o in ops:
                     if o[0] == S.B:
@@ -253,21 +262,87 @@ def test_zb1p_invariants():
                     elif o[0] == S.W:
                         assert o[1] in seen_b
                 assert [o[1] for o in ops if o[0] == S.W] == list(range(M))
-                # activation budget P-k, counted until W
-                assert S.peak_inflight(ops, split=True) <= min(P - k, M)
+                # the page's limit on micro-batches whose backward (W) is not
+                # done: p for ZB1P, 2p for ZB2P, counted until W
+                assert S.peak_inflight(ops, split=True) <= min(scale * P, M)
 
 
-def test_zb1p_never_slower_than_cost_equivalent_1f1b():
-    # With F=B=W=1 the unsplit backward costs 2 units: window 3M + 3(P-1).
-    for P in (2, 4, 8):
-        for M in (P, 4 * P, 8 * P):
-            lists, starts = S.simulate_zb(P, M, 1)
-            assert S.total_time(starts) <= 3 * M + 3 * (P - 1)
+def test_zb_limits_four_stage_example():
+    # The page's example: a 4-stage pipeline may hold 4 (ZB1P) or 8 (ZB2P)
+    # micro-batches with their backward unfinished; with enough micro-batches
+    # the greedy placement defers W until it reaches that limit.
+    for scale, limit in ((1, 4), (2, 8)):
+        lists, _ = S.simulate_zb(4, 32, scale)
+        assert [S.peak_inflight(o, split=True) for o in lists] == [limit] * 4
 
 
-def test_zb2p_budget_doubles():
-    lists, _ = S.simulate_zb(4, 32, 2)
-    assert S.peak_inflight(lists[0], split=True) <= 8
+def test_zb2p_runs_more_warmup_forwards():
+    # ZB2P does more forwards in warmup than the 1F1B order ZB1P keeps.
+    for P in (2, 3, 4, 8):
+        for M in (2 * P, 4 * P):
+            for scale in (1, 2):
+                lists, _ = S.simulate_zb(P, M, scale)
+                for k in range(P):
+                    fb = [o[0] for o in lists[k] if o[0] != S.W]
+                    nf = fb.index(S.B)
+                    if scale == 1:
+                        assert nf == P - k
+                    else:
+                        assert nf == 2 * (P - k) - 1
+                        assert nf > P - k or k == P - 1
+
+
+def test_zb_window_lower_bound():
+    # Unit costs: every stage runs 3M ops and stage P-1 cannot start before
+    # t = P-1, so no schedule of the split backward is shorter than 3M+P-1.
+    # With M >= P both ZB placements reach the bound; plain 1F1B with the
+    # whole backward (2 units) takes 3M + 3(P-1).
+    for P in (1, 2, 3, 4, 8):
+        for M in (P, 2 * P, 4 * P, 32):
+            for scale in (1, 2):
+                lists, starts = S.simulate_zb(P, M, scale)
+                assert S.total_time(starts) == 3 * M + P - 1
+            mk, _ = S.simulate_timed(S.all_stage_lists(P, M, 1, S.ONE_F_ONE_B), {S.F: 1, S.B: 2, S.W: 0})
+            assert mk == 3 * M + 3 * (P - 1)
+
+
+def test_zb2p_removes_the_bubble_zb1p_keeps_some():
+    # [GPipe->ZB ZB1P 与 ZB2P]: under equal F/B/W costs and enough
+    # micro-batches ZB2P leaves no idle slot between a stage's first and last
+    # op; ZB1P's budget limits how far W can move, so some bubble remains.
+    for P in (2, 3, 4, 5, 8):
+        for M in range(2 * P - 1, 4 * P + 1):
+            l2, s2 = S.simulate_zb(P, M, 2)
+            assert _zb_idle(l2, s2) == [0] * P, (P, M)
+            l1, s1 = S.simulate_zb(P, M, 1)
+            idle1 = _zb_idle(l1, s1)
+            assert idle1[0] > 0 and sum(idle1) > 0, (P, M)
+            # stage k starts at k and runs without a gap: it ends at 3M + k
+            for k in range(P):
+                assert s2[k][0] == k and s2[k][-1] + 1 == 3 * M + k
+    # the headline ZB shapes
+    l1, s1 = S.simulate_zb(4, 32, 1)
+    l2, s2 = S.simulate_zb(4, 32, 2)
+    assert sum(_zb_idle(l2, s2)) == 0 < sum(_zb_idle(l1, s1))
+
+
+def test_zb2p_warmup_is_tight():
+    # 2(P-k)-1 is the only warmup that removes the bubble on stages k >= 1:
+    # one forward fewer leaves stage k waiting for its first backward, one
+    # more delays that backward for the stages upstream.
+    for P in (3, 4, 8):
+        for M in (2 * P, 4 * P):
+            base = [2 * (P - k) - 1 for k in range(P)]
+            for k in range(P - 1):
+                w = list(base)
+                w[k] -= 1
+                lists, starts = S.simulate_zb(P, M, 2, warmups=w)
+                assert _zb_idle(lists, starts)[k] > 0
+                if k >= 1:
+                    w = list(base)
+                    w[k] += 1
+                    lists, starts = S.simulate_zb(P, M, 2, warmups=w)
+                    assert sum(_zb_idle(lists, starts)) > 0
 
 
 # --- slots ([1F1B §5.2] activations dict; lowest free index) -----------------
