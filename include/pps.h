@@ -56,8 +56,8 @@ extern "C" {
 
 #define PPS_GPIPE 0 /* all forwards, then all backwards in reverse order      */
 #define PPS_1F1B  1 /* synchronous 1F1B; interleaved 1F1B when v > 1         */
-#define PPS_ZB1P  2 /* 1F1B F/B order with the B/W split, budget P-k         */
-#define PPS_ZB2P  3 /* same with budget 2(P-k)                               */
+#define PPS_ZB1P  2 /* 1F1B F/B order with the B/W split, budget P            */
+#define PPS_ZB2P  3 /* 2(P-k)-1 warmup forwards, B/W split, budget 2P        */
 
 /* One entry of a stage's op list (also the layout of the executor's op log). */
 typedef struct pps_op {
@@ -84,11 +84,16 @@ typedef struct pps_op {
  *     virtual stage c*P+k; micro-batches in groups of P per chunk; warmup
  *     min(2(P-k-1) + (v-1)P + 1, M v) forwards, then alternate B and F.
  *     Needs M % P == 0.
- *   kind PPS_ZB1P / PPS_ZB2P ([GPipe->ZB ZB1P 与 ZB2P]): the 1F1B F/B order;
- *     a W op is placed wherever the stage cannot run its next F/B in the
- *     unit-cost simulation (dependency not done, or an F that would exceed
- *     the budget of P-k (ZB2P: 2(P-k)) entries counted until W); leftover
- *     W ops drain oldest-first after the last B.  v must be 1.
+ *   kind PPS_ZB1P / PPS_ZB2P ([GPipe->ZB ZB1P 与 ZB2P]): the page limits
+ *     the micro-batches a stage holds with their weight gradient not done
+ *     to p (ZB1P) or 2p (ZB2P), p = P, on every stage.  F/B order: ZB1P the
+ *     1F1B order; ZB2P warms up with min(2(P-k)-1, M) forwards (the slots
+ *     before its first backward can start when F, B and W cost the same),
+ *     then alternates B and F.  A W op is placed wherever the stage cannot
+ *     run its next F/B in the unit-cost simulation (dependency not done, or
+ *     an F that would exceed the budget, entries counted until W); leftover
+ *     W ops drain oldest-first after the last B.  With M >= 2P-1, ZB2P
+ *     leaves no idle slot between a stage's first and last op.  v must be 1.
  * Arguments: ops = caller-owned array of cap entries (may be NULL if cap==0).
  * Returns PPS_OK; PPS_EFULL if cap < *n_ops (nothing written past cap;
  * *n_ops is still set); PPS_EINVAL for P < 1, M < 1, k not in [0,P), v < 1,
@@ -169,13 +174,16 @@ typedef struct pps_stage pps_stage;
 /*
  * pps_stage_create -- build the handle for stage desc->k.
  * Computes the stage's op list with pps_make_schedule, sizes the stash pool
- * to the schedule's peak live count (P-k for 1F1B; M for GPipe) and
- * allocates, once, on the current device: the pool, scratch and the fp32
- * gradient buffers (library-owned, zeroed).  Nothing is allocated later.
- * Limits: d a multiple of 8 up to 16384, ffn a multiple of 8; with bf16
- * SwiGLU blocks every GEMM operand must stay under 2 GiB (T * 2ffn and
- * 2*ceil(ffn/32)*32 * d elements of 2 bytes), since the MFMA kernel
- * addresses operands with 32-bit offsets.
+ * to the schedule's peak live count (P-k for 1F1B; M for GPipe; P for
+ * ZB1P and up to 2P for ZB2P) and allocates, once, on the current device:
+ * the pool, scratch and the fp32 gradient buffers (library-owned, zeroed).
+ * Nothing is allocated later.
+ * Limits: P, M, v, L >= 1, 0 <= k < P, kind one of the PPS_* kinds,
+ * P*v*M <= 2^24, v*L <= 2^20 (checked before anything is allocated);
+ * d a multiple of 8 up to 16384, ffn a multiple of 8; with bf16 SwiGLU
+ * blocks every GEMM operand must stay under 2 GiB (T * 2ffn, T * d and
+ * 2*ceil(ffn/32)*32 * d elements of 2 bytes, T rounded up to 8), since the
+ * MFMA kernel addresses operands with 32-bit offsets.
  * Returns PPS_EINVAL (bad desc), PPS_ENOMEM, PPS_EHIP.  *out is set only
  * on success.
  */

@@ -180,6 +180,10 @@ Layout make_layout(const pps_stage_desc& d, bool swiglu, bool split, int es) {
 
 int validate_desc(const pps_stage_desc* d) {
     if (!d) return PPS_EINVAL;
+    // Schedule parameters first: everything below sizes host arrays from them.
+    if (d->P < 1 || d->M < 1 || d->v < 1 || d->L < 1 || d->k < 0 || d->k >= d->P) return PPS_EINVAL;
+    if (d->kind < PPS_GPIPE || d->kind > PPS_ZB2P) return PPS_EINVAL;
+    if ((long long)d->P * d->v * d->M > (1LL << 24) || (long long)d->v * d->L > (1LL << 20)) return PPS_EINVAL;
     if (d->block_type != PPS_BLOCK_SWIGLU && d->block_type != PPS_BLOCK_TOY_GELU) return PPS_EINVAL;
     if (d->dtype != PPS_DTYPE_BF16 && d->dtype != PPS_DTYPE_FP32) return PPS_EINVAL;
     if (d->block_type == PPS_BLOCK_TOY_GELU && d->dtype != PPS_DTYPE_FP32) return PPS_EINVAL;
@@ -192,11 +196,12 @@ int validate_desc(const pps_stage_desc* d) {
     if (d->block_type == PPS_BLOCK_SWIGLU && d->dtype == PPS_DTYPE_BF16) {
         // The MFMA GEMM addresses each operand with 32-bit byte offsets: the
         // largest ones (dg|du [T, 2 ffn] and its T-contiguous copy, rows
-        // padded to a multiple of 8; the interleaved gate/up weight copy)
-        // must stay under 2 GiB.
+        // padded to a multiple of 8; the [T, d] operands and their copies;
+        // the interleaved gate/up weight copy) must stay under 2 GiB.
         const double lim = 2147483648.0, Tp = (double)((d->T + 7) / 8 * 8);
         const double f2 = 2.0 * (double)d->ffn, rows = (double)pps::swiglu_b_rows(d->ffn);
-        if (Tp * f2 * 2 >= lim || rows * (double)d->d * 2 >= lim) return PPS_EINVAL;
+        if (Tp * f2 * 2 >= lim || Tp * (double)d->d * 2 >= lim || rows * (double)d->d * 2 >= lim)
+            return PPS_EINVAL;
     }
     if ((d->flags & PPS_FLAG_PROFILE) && d->profile_capacity < 0) return PPS_EINVAL;
     if (!(d->flags & PPS_FLAG_BOOKKEEPING_ONLY)) {

@@ -253,6 +253,28 @@ def test_create_rejects_bad_descs():
     with pytest.raises(pps.PpsError):
         _bk_stage(8, 16, 0, d=16384, ffn=65536, T=8)        # interleaved gate/up copy 4.3 GB
     _bk_stage(8, 16, 0, d=8192, ffn=28672, T=32768, dtype=pps.DTYPE_FP32)   # the fp32 path has no such limit
+    with pytest.raises(pps.PpsError):
+        _bk_stage(8, 16, 0, d=16384, ffn=4096, T=100000)    # the [T, d] operands: 3.28 GB
+
+
+def test_create_rejects_bad_schedule_params_before_allocating():
+    # Called through the C ABI with (fake, never dereferenced) weight pointers
+    # so the weight-table copy would run if the range checks did not come first.
+    L = _lib_or_skip()
+    fake = (ctypes.c_void_p * 64)(*([0x1000] * 64))
+    base = dict(P=4, M=8, k=0, v=1, kind=pps.ONE_F_ONE_B, block_type=pps.BLOCK_SWIGLU, dtype=pps.DTYPE_BF16,
+                L=2, d=64, ffn=128, T=16)
+    bad = [dict(v=-1), dict(v=0), dict(P=0), dict(M=0), dict(L=0), dict(L=-3), dict(k=-1), dict(k=4),
+           dict(kind=7), dict(kind=-1), dict(P=1 << 12, M=1 << 13), dict(v=1 << 11, L=1 << 10, P=1, M=1)]
+    for over in bad:
+        desc = pps.PpsStageDesc()
+        for key, val in {**base, **over}.items():
+            setattr(desc, key, val)
+        desc.eps = 1e-6
+        desc.weights = ctypes.cast(fake, ctypes.POINTER(ctypes.c_void_p))
+        h = ctypes.c_void_p()
+        assert L.pps_stage_create(ctypes.byref(desc), ctypes.byref(h)) == pps.EINVAL, over
+        assert not h.value
 
 
 def test_simulate_pipeline_matches_oracle():
