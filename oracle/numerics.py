@@ -110,6 +110,50 @@ def swiglu_backward(s, dy, p):
     return dx, grads
 
 
+def swiglu_block_at(x, dy, p, rows, wsel, gsel, eps=EPS):
+    """One SwiGLU block's forward and backward, evaluated only where asked.
+
+    The same definitions as ``swiglu_forward`` / ``swiglu_backward``, for
+    blocks too wide to evaluate whole in float64 on the host:
+
+    * ``rows``: token indices; y and dx are token-local, so their rows need
+      only the sampled tokens' inputs.
+    * ``wsel``: {"Wg"|"Wu"|"Wd": (I, J)}; dW[I][:, J] is a sum over every
+      token, so it needs every token's n (or h) at the columns I and dg/du (or
+      dy) at the columns J.
+    * ``gsel``: feature indices K; dgamma[K] needs every token's dn at K,
+      which needs every token's dg and du in full.
+
+    Returns (y_rows, dx_rows, {"Wg"|"Wu"|"Wd": dW block}, dgamma_at_K).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    d = x.shape[1]
+    y_rows, s = swiglu_forward(x[rows], p, eps)
+    dx_rows, _, _ = swiglu_backward_input(s, dy[rows], p)
+
+    # every token: g, u (and h), dh, then dg, du
+    n, r = rmsnorm_forward(x, p["gamma"], eps)
+    g = n @ p["Wg"]
+    u = n @ p["Wu"]
+    h = silu(g) * u
+    dh = dy @ p["Wd"].T
+    sg = sigmoid(g)
+    du = dh * g * sg
+    dg = dh * u * sg * (1.0 + g * (1.0 - sg))
+    dW = {}
+    for key, (I, J) in wsel.items():
+        if key == "Wd":
+            dW[key] = h[:, I].T @ dy[:, J]
+        elif key == "Wg":
+            dW[key] = n[:, I].T @ dg[:, J]
+        else:
+            dW[key] = n[:, I].T @ du[:, J]
+    dn_k = dg @ p["Wg"][gsel, :].T + du @ p["Wu"][gsel, :].T
+    dgamma = np.sum(dn_k * x[:, gsel] * r[:, None], axis=0)
+    return y_rows, dx_rows, dW, dgamma
+
+
 # ---------------------------------------------------------------------------
 # Toy block: Linear (with bias) + exact GELU
 # ---------------------------------------------------------------------------

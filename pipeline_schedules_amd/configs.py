@@ -73,7 +73,7 @@ C4_INTERLEAVED = C3_SLICE.with_(name="c4_80layer_p8_v2", v=2, L=5)
 C5_ZB = StageConfig("c5_zb1p_p4m32", P=4, M=32, k=0, v=1, kind="zb1p",
                     block="swiglu", dtype="bf16", L=8, d=4096, f=14336, T=8192)
 
-# The same stage under ZB2P (W budget 2(P-k), larger stash).
+# The same stage under ZB2P (2(P-k)-1 warmup forwards, W budget 2P, larger stash).
 C6_ZB2P = C5_ZB.with_(name="c6_zb2p_p4m32", kind="zb2p")
 
 # The same stage unsplit (plain 1F1B): the reference point for the cost of the split.

@@ -1,0 +1,203 @@
+"""Dense GPU parity at the 80-layer-slice widths against the float64 oracle.
+
+Two checks with every token non-zero, so every weight-gradient GEMM reduces
+over dense tokens and the fp32 in-place accumulation runs on real data
+([Sched §09]: compare the pipelined gradients with the un-pipelined ones;
+[1F1B §4.5]: synchronous 1F1B is the large-batch SGD step):
+
+* the whole stage -- 10 blocks, d=8192, ffn=28672, P=8, M=16, k=0, 1F1B --
+  at 256 tokens per micro-batch, compared block by block with the oracle's
+  full-batch step: y and dx of every micro-batch, dgamma of every block in
+  full, and a 64 x 64 block of every weight gradient (all 4096 tokens);
+* one block at the benchmark's full micro-batch (8192 tokens, two
+  micro-batches) in the launch configuration the benchmark times, for the
+  80-layer slice (1F1B) and the Zero-Bubble stage (d=4096, ffn=14336, ZB1P):
+  y and dx on sampled rows, weight gradients on sampled 64 x 64 blocks and
+  dgamma on sampled features, each a sum over all 16384 tokens.
+
+Inputs: the seeded device generator the benchmark uses (x ~ N(0,1), weights
+~ N(0,0.02), output gradients ~ N(0,0.01)), gamma ~ 1 + N(0,0.1).
+Tolerance: rel-L2 <= 2e-2 per tensor (bf16).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import numerics as N
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+NSEL = 64
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from pipeline_schedules_amd import pps
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pps.lib()
+    return torch, pps
+
+
+def _host(t):
+    return t.detach().double().cpu().numpy()
+
+
+def _inputs(torch, cfg):
+    from pipeline_schedules_amd.inputs import make_device_inputs
+    dev = torch.device("cuda:0")
+    inp = make_device_inputs(cfg, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed + 101)
+    for p in inp["params"]:
+        p["gamma"] = (1.0 + 0.1 * torch.randn((cfg.d,), generator=gen, device=dev)).float()
+    return inp
+
+
+def _run(env, cfg, inp):
+    torch, pps = env
+    weights = []
+    for p in inp["params"]:
+        weights += [p["Wg"], p["Wu"], p["Wd"], p["gamma"]]
+    st = pps.stage_from_config(cfg, weights=weights, stream=torch.cuda.current_stream())
+    ops = pps.make_schedule(cfg.P, cfg.M, cfg.k, cfg.v, pps.KIND_BY_NAME[cfg.kind])
+    ys = [torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda") for _ in range(cfg.M)]
+    dxs = [torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda") for _ in range(cfg.M)]
+    st.zero_grad()
+    for op, mb, c, *_ in ops:
+        if op == pps.OP_F:
+            st.forward(mb, c, inp["xs"][mb], ys[mb])
+        elif op == pps.OP_B:
+            st.backward(mb, c, inp["Gs"][mb], dxs[mb])
+        else:
+            st.backward_weight(mb, c)
+    st.sync()
+    assert st.oplog() == ops
+    return st, ys, dxs
+
+
+def _selections(cfg, seed):
+    rng = np.random.default_rng(seed)
+    pick = lambda n: np.sort(rng.choice(n, NSEL, replace=False))
+    return {"Wg": (pick(cfg.d), pick(cfg.f)), "Wu": (pick(cfg.d), pick(cfg.f)), "Wd": (pick(cfg.f), pick(cfg.d))}
+
+
+def _grad_blocks(torch, st, cfg, b, wsel):
+    out = {}
+    for key, which, shape in (("Wg", 0, (cfg.d, cfg.f)), ("Wu", 1, (cfg.d, cfg.f)), ("Wd", 2, (cfg.f, cfg.d))):
+        I, J = wsel[key]
+        g = st.grad(0, b, which, shape)
+        out[key] = _host(g[torch.from_numpy(I).cuda()][:, torch.from_numpy(J).cuda()])
+    out["gamma"] = _host(st.grad(0, b, 3, (cfg.d,)))
+    return out
+
+
+def _host_params(p):
+    return {k: _host(v) for k, v in p.items()}
+
+
+def _report(name, errs):
+    print(name, " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= TOL}
+    assert not bad, f"rel-L2 above {TOL}: {bad}"
+
+
+# ---------------------------------------------------------------------------
+# the whole 10-block stage, 16 micro-batches, 256 dense tokens each
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def c3_stage(env):
+    """GPU results of the full stage, plus the oracle's forward (block by
+    block, keeping what the backward needs)."""
+    torch, pps = env
+    from pipeline_schedules_amd.configs import StageConfig
+    cfg = StageConfig("c3-dense-T256", P=8, M=16, k=0, v=1, kind="1f1b", block="swiglu", dtype="bf16",
+                      L=10, d=8192, f=28672, T=256)
+    inp = _inputs(torch, cfg)
+    st, ys, dxs = _run(env, cfg, inp)
+    wsel = [_selections(cfg, 1000 + b) for b in range(cfg.L)]
+    gpu = {"y": [_host(y) for y in ys], "dx": [_host(x) for x in dxs],
+           "grads": [_grad_blocks(torch, st, cfg, b, wsel[b]) for b in range(cfg.L)]}
+    st.close()
+    del ys, dxs
+
+    # oracle forward of the full batch (the micro-batches stacked), block by block
+    X = np.concatenate([_host(x) for x in inp["xs"]], axis=0)
+    saved = []
+    for b in range(cfg.L):
+        p = _host_params(inp["params"][b])
+        X, s = N.swiglu_forward(X, p, cfg.eps)
+        keep = {"x": s["x"], "r": s["r"], "g": s["g"], "u": s["u"], "n": None, "h": None,
+                "n_g": s["n"][:, wsel[b]["Wg"][0]], "n_u": s["n"][:, wsel[b]["Wu"][0]],
+                "h_d": s["h"][:, wsel[b]["Wd"][0]]}
+        saved.append(keep)
+        del s, p
+    return {"cfg": cfg, "inp": inp, "gpu": gpu, "wsel": wsel, "saved": saved, "Y": X}
+
+
+def test_c3_dense_forward(c3_stage):
+    cfg, gpu, Y = c3_stage["cfg"], c3_stage["gpu"], c3_stage["Y"]
+    ry = np.split(Y, cfg.M)
+    _report("c3-dense y", {f"y{i}": N.rel_l2(gpu["y"][i], ry[i]) for i in range(cfg.M)})
+
+
+def test_c3_dense_backward(c3_stage):
+    cfg, gpu, inp, wsel, saved = (c3_stage[k] for k in ("cfg", "gpu", "inp", "wsel", "saved"))
+    DY = np.concatenate([_host(g) for g in inp["Gs"]], axis=0)
+    errs = {}
+    for b in reversed(range(cfg.L)):
+        p = _host_params(inp["params"][b])
+        s = saved[b]
+        DY_in = DY
+        DY, ws, dgam = N.swiglu_backward_input(s, DY_in, p)
+        ref = {"Wg": s["n_g"].T @ ws["dg"][:, wsel[b]["Wg"][1]],
+               "Wu": s["n_u"].T @ ws["du"][:, wsel[b]["Wu"][1]],
+               "Wd": s["h_d"].T @ DY_in[:, wsel[b]["Wd"][1]],
+               "gamma": dgam}
+        for key in ref:
+            errs[f"d{key}{b}"] = N.rel_l2(gpu["grads"][b][key], ref[key])
+        del ws, p
+        saved[b] = None
+    rdx = np.split(DY, cfg.M)
+    for i in range(cfg.M):
+        errs[f"dx{i}"] = N.rel_l2(gpu["dx"][i], rdx[i])
+    _report("c3-dense backward", errs)
+
+
+# ---------------------------------------------------------------------------
+# one block at the full micro-batch, in the benchmark's launch configuration
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,d,f,kind,P", [("c3-block-T8192", 8192, 28672, "1f1b", 8),
+                                             ("c5-block-T8192", 4096, 14336, "zb1p", 4)])
+def test_full_microbatch_block_dense(env, name, d, f, kind, P):
+    torch, pps = env
+    from pipeline_schedules_amd.configs import StageConfig
+    cfg = StageConfig(name, P=P, M=2, k=0, v=1, kind=kind, block="swiglu", dtype="bf16", L=1, d=d, f=f, T=8192)
+    inp = _inputs(torch, cfg)
+    st, ys, dxs = _run(env, cfg, inp)
+    wsel = _selections(cfg, 77)
+    got = _grad_blocks(torch, st, cfg, 0, wsel)
+    st.close()
+    rng = np.random.default_rng(5)
+    gsel = np.sort(rng.choice(cfg.d, 256, replace=False))
+    p = _host_params(inp["params"][0])
+    errs = {}
+    ref_w = {k: 0.0 for k in wsel}
+    ref_g = 0.0
+    for i in range(cfg.M):
+        rows = np.sort(np.concatenate([rng.choice(cfg.T - 1, 31, replace=False), [cfg.T - 1]]))
+        y_r, dx_r, dW, dgam = N.swiglu_block_at(_host(inp["xs"][i]), _host(inp["Gs"][i]), p, rows, wsel, gsel,
+                                                cfg.eps)
+        idx = torch.from_numpy(rows).cuda()
+        errs[f"y{i}"] = N.rel_l2(_host(ys[i][idx]), y_r)
+        errs[f"dx{i}"] = N.rel_l2(_host(dxs[i][idx]), dx_r)
+        for k in wsel:
+            ref_w[k] = ref_w[k] + dW[k]
+        ref_g = ref_g + dgam
+    for k in wsel:
+        errs[f"d{k}"] = N.rel_l2(got[k], ref_w[k])
+    errs["dgamma"] = N.rel_l2(got["gamma"][gsel], ref_g)
+    _report(name, errs)

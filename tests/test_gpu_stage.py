@@ -188,11 +188,17 @@ def test_toy_stage_parity(env, kind):
     _check(C1_TOY, got, inp, TOL["fp32"])
 
 
+@pytest.mark.parametrize("shape", ["ragged", "full_tiles"])
 @pytest.mark.parametrize("recompute", [False, True])
-def test_interleaved_stage_parity(env, recompute):
+def test_interleaved_stage_parity(env, recompute, shape):
+    # "full_tiles": T and ffn multiples of the 256 x 256 GEMM tile, so the dh
+    # epilogue writes h transposed for dW_d under chunked stashing.
     torch, pps, G = env
     from pipeline_schedules_amd.inputs import make_inputs
-    cfg = _swiglu_cfg("bf16", T=264, d=264, f=392, L=1, M=4, P=2, k=0, v=2)
+    if shape == "ragged":
+        cfg = _swiglu_cfg("bf16", T=264, d=264, f=392, L=1, M=4, P=2, k=0, v=2)
+    else:
+        cfg = _swiglu_cfg("bf16", T=512, d=264, f=512, L=2, M=4, P=2, k=0, v=2)
     inp = make_inputs(cfg, gamma="random")
     rng = np.random.default_rng(5)
     # independent seeded inputs for chunk 1 (its real input comes from another device)
@@ -209,13 +215,14 @@ def test_interleaved_stage_parity(env, recompute):
     assert st.oplog() == ops
     assert st.stats()["peak_live_entries"] == max(o[4] for o in ops)
     for c, (cx, cg) in enumerate([(inp.xs, inp.Gs), (xs1, gs1)]):
-        ry, rdx, rg = N.full_batch_step(cx, cg, [inp.params[0][c]], "swiglu", cfg.eps)
+        ry, rdx, rg = N.full_batch_step(cx, cg, inp.params[0][c * cfg.L:(c + 1) * cfg.L], "swiglu", cfg.eps)
         for i in range(cfg.M):
             assert N.rel_l2(G.to_host(ys[c][i]), ry[i]) <= TOL["bf16"]
             assert N.rel_l2(G.to_host(dxs[c][i]), rdx[i]) <= TOL["bf16"]
-        got = G.stage_grads(st, 1, "swiglu", cfg.d, cfg.f, chunk=c)
-        for key in rg[0]:
-            assert N.rel_l2(got[0][key], rg[0][key]) <= TOL["bf16"], (c, key)
+        got = G.stage_grads(st, cfg.L, "swiglu", cfg.d, cfg.f, chunk=c)
+        for b in range(cfg.L):
+            for key in rg[b]:
+                assert N.rel_l2(got[b][key], rg[b][key]) <= TOL["bf16"], (c, b, key)
     st.close()
 
 

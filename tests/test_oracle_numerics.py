@@ -54,6 +54,31 @@ def test_swiglu_backward_matches_autograd(T, d, f):
         np.testing.assert_allclose(grads[k], tp[k].grad.numpy(), rtol=1e-10, atol=1e-12)
 
 
+def test_swiglu_block_at_matches_autograd():
+    # The entry-sampled evaluation used at full width equals torch.autograd's
+    # gradients of the same block at those entries (rows of y and dx, blocks
+    # of every dW, entries of dgamma).
+    rng = np.random.default_rng(11)
+    T, d, f = 29, 16, 24
+    p = _rand_swiglu(rng, d, f)
+    x = rng.normal(0, 1, (T, d))
+    dy = rng.normal(0, 1, (T, d))
+    tp = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in p.items()}
+    tx = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    ty = _torch_swiglu(tx, tp, 1e-3)
+    ty.backward(torch.tensor(dy, dtype=torch.float64))
+    rows = np.array([0, 3, 17, 28])
+    wsel = {"Wg": (np.array([1, 5, 15]), np.array([0, 7, 23])), "Wu": (np.array([2, 9]), np.array([4, 11, 20])),
+            "Wd": (np.array([0, 13, 22]), np.array([3, 15]))}
+    gsel = np.array([0, 6, 15])
+    y_r, dx_r, dW, dgam = N.swiglu_block_at(x, dy, p, rows, wsel, gsel, eps=1e-3)
+    np.testing.assert_allclose(y_r, ty.detach().numpy()[rows], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dx_r, tx.grad.numpy()[rows], rtol=1e-10, atol=1e-12)
+    for k, (I, J) in wsel.items():
+        np.testing.assert_allclose(dW[k], tp[k].grad.numpy()[np.ix_(I, J)], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dgam, tp["gamma"].grad.numpy()[gsel], rtol=1e-10, atol=1e-12)
+
+
 def test_toy_backward_matches_autograd():
     rng = np.random.default_rng(2)
     p = {"W": rng.normal(0, 0.5, (6, 6)), "b": rng.normal(0, 0.5, (6,))}
