@@ -49,6 +49,15 @@ __device__ __forceinline__ void swiglu_bwd_f(float dh, float g, float u, float& 
     dg = dh * u * s * (1.0f + g * (1.0f - s));
 }
 
+// Both at once with one sigmoid: h = silu(g) u, and dg, du for dh.  Same
+// expressions, so the same bits, as swiglu_f and swiglu_bwd_f.
+__device__ __forceinline__ void swiglu_h_bwd_f(float dh, float g, float u, float& h, float& dg, float& du) {
+    const float s = sigmoid_f(g);
+    h = g * s * u;
+    du = dh * g * s;
+    dg = dh * u * s * (1.0f + g * (1.0f - s));
+}
+
 // Exact (erf-based) GELU and its derivative Phi(z) + z phi(z).
 __device__ __forceinline__ float gelu_f(float z) {
     return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));

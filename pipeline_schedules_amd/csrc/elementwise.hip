@@ -83,12 +83,14 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const S* __restrict__ 
     for (int q = 0; q < Q; ++q) {
         const int64_t c = threadIdx.x + 256 * q;
         if (c < nchunk) {
-            float gm[8], o[8];
-            Vec8<float>::load(gamma + c * 8, gm);
             if (xcopy) Vec8<S>::store(xcopy + row * d + c * 8, v[q]);
+            if (n) {
+                float gm[8], o[8];
+                Vec8<float>::load(gamma + c * 8, gm);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = (v[q][i] * rr) * gm[i];
-            Vec8<S>::store(n + row * d + c * 8, o);
+                for (int i = 0; i < 8; ++i) o[i] = (v[q][i] * rr) * gm[i];
+                Vec8<S>::store(n + row * d + c * 8, o);
+            }
         }
     }
 }
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ a
 // (gate/up interleave of the forward weight copy).
 __global__ __launch_bounds__(256) void tile_transpose_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
                                                              int64_t lds, uint16_t* __restrict__ dst, int64_t ldd,
-                                                             int grp, int half) {
+                                                             int grp, int half, const float* __restrict__ rowscale) {
     __shared__ float tile[64][65];
     const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
     const int t = threadIdx.x;
@@ -247,6 +249,11 @@ __global__ __launch_bounds__(256) void tile_transpose_kernel(const uint16_t* __r
         float v[8];
         if (row < rows && col < cols) {
             Vec8<uint16_t>::load(src + row * lds + col, v);
+            if (rowscale) {
+                const float sc = rowscale[row];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] *= sc;   // rounded to bf16 by the store
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] = 0.0f;
@@ -382,12 +389,12 @@ hipError_t colsum_acc(const float* a, int64_t T, int64_t d, float* out, hipStrea
 }
 
 hipError_t transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t lds, void* dst, int64_t ldd, int grp,
-                          int half, hipStream_t s) {
+                          int half, hipStream_t s, const float* rowscale) {
     if (cols <= 0 || ldd <= 0) return hipSuccess;
     if (cols % 8 || ldd % 8 || lds % 8) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((ldd + 63) / 64), (unsigned)((cols + 63) / 64));
     hipLaunchKernelGGL(tile_transpose_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), rows, cols, lds,
-                       static_cast<uint16_t*>(dst), ldd, grp, half);
+                       static_cast<uint16_t*>(dst), ldd, grp, half, rowscale);
     return hipGetLastError();
 }
 

@@ -118,17 +118,15 @@ struct EpiPtr {
     char* o2;
 };
 
-// Gate/up pair for hidden columns col..col+3: stores g, u (bf16) and
-// h = silu(g) u computed from the stored values.
+// Gate/up pair for hidden columns col..col+3, already scaled by the row's
+// RMSNorm factor: stores g, u (bf16, for the backward) and h = silu(g) u
+// computed from the fp32 values (the down GEMM's operand).
 __device__ __forceinline__ void epi4_swiglu(const EpiPtr& a, const float (&g)[4], const float (&u)[4]) {
-    const uint2 gp = pack4(g), up = pack4(u);
-    float gs[4], us[4], hh[4];
-    unpack4(gp, gs);
-    unpack4(up, us);
+    float hh[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) hh[k] = swiglu_f(gs[k], us[k]);
-    *reinterpret_cast<uint2*>(a.o0) = gp;
-    *reinterpret_cast<uint2*>(a.o1) = up;
+    for (int k = 0; k < 4; ++k) hh[k] = swiglu_f(g[k], u[k]);
+    *reinterpret_cast<uint2*>(a.o0) = pack4(g);
+    *reinterpret_cast<uint2*>(a.o1) = pack4(u);
     *reinterpret_cast<uint2*>(a.o2) = pack4(hh);
 }
 
@@ -193,10 +191,7 @@ __device__ __forceinline__ void epi8_swiglu_bwd(const EpiPtr& a, const float (&w
     unpack8(in.g, g);
     unpack8(in.u, u);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        swiglu_bwd_f(w[k], g[k], u[k], dg[k], du[k]);
-        hh[k] = swiglu_f(g[k], u[k]);
-    }
+    for (int k = 0; k < 8; ++k) swiglu_h_bwd_f(w[k], g[k], u[k], hh[k], dg[k], du[k]);
     *reinterpret_cast<uint4*>(a.o0) = pack8(dg);
     *reinterpret_cast<uint4*>(a.o1) = pack8(du);
 }
@@ -235,6 +230,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     const int64_t n0 = (int64_t)tn * (p.swiglu ? BN / 2 : BN);   // first output column
     const int64_t nb0 = (int64_t)tn * BN;                         // first B row
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    // Epilogue rows of this lane: lr + 16 i + 0..3 (see the epilogue below).
+    const int lr = wm * 128 + 4 * (lane >> 4);
 
     // Loader: each wavefront moves NQ pieces of 1 KB per operand tile; piece q
     // holds LDS rows (wave*NQ+q)*8 .. +7, lane l row + l/8 at position l&7,
@@ -406,8 +403,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     // (i, j) is output row lr + 16i + r, column lc + j: each lane holds eight
     // consecutive columns of a row (SwiGLU: gate tiles j < 4 and up tiles
     // j >= 4 of the four hidden columns lc .. lc+3).
-    const int lr = wm * 128 + 4 * (lane >> 4);
     const int lc = p.swiglu ? wn * 64 + 4 * (lane & 15) : wn * 128 + 8 * (lane & 15);
+    // SwiGLU: the RMSNorm factor r of this lane's 32 output rows (the GEMM
+    // read x; gamma is folded into B), requested first.
+    float rsc[8][4];
+    if constexpr (EPI == EPI_SWIGLU) {
+        const float* rs = p.e.rowscale;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t row = m0 + lr + 16 * i;
+            if (rs && row + 3 < p.M) {
+                const float4 v = *reinterpret_cast<const float4*>(rs + row);
+                rsc[i][0] = v.x; rsc[i][1] = v.y; rsc[i][2] = v.z; rsc[i][3] = v.w;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) rsc[i][k] = rs && row + k < p.M ? rs[row + k] : 1.0f;
+            }
+        }
+    }
     const EpiArgs e = p.e;
     const int64_t pM = p.M, pN = p.N;
     constexpr int ESO = (EPI == EPI_STORE_F32 || EPI == EPI_ACC_F32) ? 4 : 2;   // output element bytes
@@ -475,8 +488,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
             if constexpr (FAST) return true;
             else return m0 + lr + i * 16 + r < pM && n0 + lc < pN;
         };
-        // inputs of row group i + 1 load while row group i computes
-        EpiIn8<EPI> in[2][4];
+        // inputs of row groups i+1 .. i+NB-1 load while row group i computes
+        // (the K loop's fragment registers are free by now)
+        constexpr int NB = EPI == EPI_SWIGLU_BWD ? 4 : EPI == EPI_ACC_F32 ? 3 : 2;
+        EpiIn8<EPI> in[NB][4];
         auto prefetch = [&](int i, EpiIn8<EPI> (&dst)[4]) __attribute__((always_inline)) {
             if constexpr (HAS_IN) {
 #pragma unroll
@@ -484,10 +499,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
                     if (ok(i, r)) epi_load8<EPI>(ptr(i, r), dst[r]);
             }
         };
-        prefetch(0, in[0]);
+#pragma unroll
+        for (int i = 0; i < NB - 1; ++i) prefetch(i, in[i]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            if (i + 1 < 8) prefetch(i + 1, in[(i + 1) & 1]);
+            if (i + NB - 1 < 8) prefetch(i + NB - 1, in[(i + NB - 1) % NB]);
             float hh[4][8];   // SwiGLU backward: h of this row group
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -495,16 +511,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
                     float w[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) w[j] = acc[i][j][r];
-                    if (ok(i, r)) epi8_swiglu_bwd(ptr(i, r), w, in[i & 1][r], hh[r]);
+                    if (ok(i, r)) epi8_swiglu_bwd(ptr(i, r), w, in[i % NB][r], hh[r]);
                 } else if constexpr (EPI == EPI_SWIGLU) {
-                    const float g[4] = {acc[i][0][r], acc[i][1][r], acc[i][2][r], acc[i][3][r]};
-                    const float u[4] = {acc[i][4][r], acc[i][5][r], acc[i][6][r], acc[i][7][r]};
+                    const float sc = rsc[i][r];
+                    const float g[4] = {acc[i][0][r] * sc, acc[i][1][r] * sc, acc[i][2][r] * sc, acc[i][3][r] * sc};
+                    const float u[4] = {acc[i][4][r] * sc, acc[i][5][r] * sc, acc[i][6][r] * sc, acc[i][7][r] * sc};
                     if (ok(i, r)) epi4_swiglu(ptr(i, r), g, u);
                 } else {
                     float w[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) w[j] = acc[i][j][r];
-                    if (ok(i, r)) epi8<EPI>(ptr(i, r), w, in[i & 1][r]);
+                    if (ok(i, r)) epi8<EPI>(ptr(i, r), w, in[i % NB][r]);
                 }
             }
             if constexpr (EPI == EPI_SWIGLU_BWD && FAST) {
@@ -565,7 +582,7 @@ hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
         return hipErrorInvalidValue;   // h is written transposed from full tiles only
     const uintptr_t ptrs = reinterpret_cast<uintptr_t>(a.e.out0) | reinterpret_cast<uintptr_t>(a.e.out1) |
                            reinterpret_cast<uintptr_t>(a.e.out2) | reinterpret_cast<uintptr_t>(a.e.in0) |
-                           reinterpret_cast<uintptr_t>(a.e.in1);
+                           reinterpret_cast<uintptr_t>(a.e.in1) | reinterpret_cast<uintptr_t>(a.e.rowscale);
     if (ptrs % 16) return hipErrorInvalidValue;
     Params p{};
     p.M = a.M;

@@ -18,7 +18,8 @@ namespace pps {
 enum Epi {
     EPI_STORE_F32 = 0,   // out0[m*ld0+n] = acc                           (float)
     EPI_RESID = 1,       // out0[m*ld0+n] = in0[m*ldi0+n] + acc           (storage type)
-    EPI_SWIGLU = 2,      // g,u pair -> out0=g, out1=u, out2=h=silu(g)*u  (storage type, ld0)
+    EPI_SWIGLU = 2,      // g,u pair -> out0=g, out1=u, out2=h=silu(g)*u  (storage type, ld0);
+                         // bf16 GEMM: g, u = rowscale[m] * acc first, h from the unrounded g, u
     EPI_SWIGLU_BWD = 3,  // dh=acc; g=in0,u=in1 (ldi0) -> out0[m*ld0+n]=dg, out0[..+nsplit]=du,
                          // and if out2: h = silu(g) u at out2[m*ldi0+n] (fp32 GEMM) or
                          // out2[n*ld2+m] (bf16 GEMM)
@@ -40,6 +41,7 @@ struct EpiArgs {
     const float* bias = nullptr;
     int64_t ld2 = 0;   // SwiGLU backward, bf16 GEMM: h is written transposed, out2[n*ld2 + m]
                        // (needs M and N multiples of 256, ld2 % 4 == 0)
+    const float* rowscale = nullptr;   // SwiGLU, bf16 GEMM: per output row factor (RMSNorm r)
 };
 
 struct GemmSeg {
@@ -64,8 +66,10 @@ struct GemmArgs {
 // dtype: PPS_DTYPE_BF16 (MFMA) or PPS_DTYPE_FP32.  Returns a hipError_t.
 hipError_t gemm(int dtype, const GemmArgs& a, hipStream_t s);
 
-// r[t] = (mean_j x[t,j]^2 + eps)^-1/2;  n[t,j] = x[t,j] r[t] gamma[j];
-// xcopy (optional) receives x.  One workgroup per row.
+// r[t] = (mean_j x[t,j]^2 + eps)^-1/2;  n[t,j] = x[t,j] r[t] gamma[j] (skipped
+// when n is null: the bf16 forward folds gamma into its weight copy and applies
+// r in the gate/up GEMM's epilogue); xcopy (optional) receives x.  One
+// workgroup per row.
 hipError_t rmsnorm_fwd(int dtype, const void* x, const float* gamma, float eps,
                        int64_t T, int64_t d, float* r, void* n, void* xcopy, hipStream_t s);
 
@@ -91,12 +95,12 @@ hipError_t gelu_bwd(const float* dy, const float* z, int64_t count, float* dz, h
 // out[j] += sum_t a[t, j]  (fp32, fixed order)
 hipError_t colsum_acc(const float* a, int64_t T, int64_t d, float* out, hipStream_t s);
 
-// Tiled bf16 transpose: dst[map(c), r] = src[r, c] for r < rows, c < cols;
-// dst columns in [rows, ldd) are zeroed.  map(c) = c, or
-// (c/grp)*2grp + half*grp + c%grp with grp > 0.  cols, lds and ldd must be
-// multiples of 8.
+// Tiled bf16 transpose: dst[map(c), r] = src[r, c] (times rowscale[r] when
+// given, rounded to bf16) for r < rows, c < cols; dst columns in [rows, ldd)
+// are zeroed.  map(c) = c, or (c/grp)*2grp + half*grp + c%grp with grp > 0.
+// cols, lds and ldd must be multiples of 8.
 hipError_t transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t lds, void* dst, int64_t ldd, int grp,
-                          int half, hipStream_t s);
+                          int half, hipStream_t s, const float* rowscale = nullptr);
 
 // Rows of the interleaved gate/up weight copy used by the forward GEMM.
 int64_t swiglu_b_rows(int64_t ffn);

@@ -253,18 +253,21 @@ double gemm_flops(double M, double N, double K) { return 2.0 * M * N * K; }
 // ---- SwiGLU block sequences ------------------------------------------------
 
 // bf16 path: refresh the K-contiguous copies of the forward weights from the
-// caller's Wg, Wu ([d, ffn]) and Wd ([ffn, d]).  Done once at the start of
-// every pass, so weights updated between passes are picked up.
+// caller's Wg, Wu ([d, ffn]), gamma ([d]) and Wd ([ffn, d]).  Done once at the
+// start of every pass, so weights updated between passes are picked up.  The
+// RMSNorm scale gamma is folded into the gate/up copy: g = (x r gamma) Wg =
+// r (x (gamma Wg)), with r applied per row in the GEMM's epilogue.
 int refresh_weight_copies(pps_stage* h) {
     const pps_stage_desc& D = h->d;
     const int64_t d = D.d, f = D.ffn;
     for (int i = 0; i < D.v * D.L; ++i) {
         const void* const* wb = h->w.data() + (size_t)i * 4;
+        const float* gamma = static_cast<const float*>(wb[3]);
         char* wgu = h->wcopy + h->wgu_off[i];
         char* wdt = h->wcopy + h->wd_off[i];
-        PPS_TRY(timed(h, PPS_K_COPY, 0.0, 4.0 * d * f * 2, [&] {
-            hipError_t e = pps::transpose_bf16(wb[0], d, f, f, wgu, d, 32, 0, h->stream);
-            if (e == hipSuccess) e = pps::transpose_bf16(wb[1], d, f, f, wgu, d, 32, 1, h->stream);
+        PPS_TRY(timed(h, PPS_K_COPY, 0.0, 4.0 * d * f * 2 + 2.0 * d * 4, [&] {
+            hipError_t e = pps::transpose_bf16(wb[0], d, f, f, wgu, d, 32, 0, h->stream, gamma);
+            if (e == hipSuccess) e = pps::transpose_bf16(wb[1], d, f, f, wgu, d, 32, 1, h->stream, gamma);
             return e;
         }));
         PPS_TRY(timed(h, PPS_K_COPY, 0.0, 2.0 * d * f * 2, [&] {
@@ -295,17 +298,25 @@ int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_
         char* ub = ab + h->lay.u[b];
         const bool copy_in = b == 0 && !recompute;
         const void* xin = copy_in ? x_in : xb;
-        // r and n = x r gamma ([T,d]); block 0 also copies x into the stash.
-        PPS_TRY(timed(h, PPS_K_RMSNORM_FWD, 0.0, (double)T * d * es * (copy_in ? 3 : 2) + T * 4.0 + d * 4.0, [&] {
-            return pps::rmsnorm_fwd(dt, xin, gamma, D.eps, T, d, rb, sn, copy_in ? xb : nullptr, h->stream);
+        // RMSNorm: r per row; block 0 also copies x into the stash.  bf16: the
+        // gate/up GEMM reads x and applies r in its epilogue (gamma is in the
+        // weight copy), so n is not formed; fp32: n = x r gamma ([T,d]).
+        const double norm_bytes = h->tn ? (double)T * d * es * (copy_in ? 2 : 1) + T * 4.0
+                                        : (double)T * d * es * (copy_in ? 3 : 2) + T * 4.0 + d * 4.0;
+        PPS_TRY(timed(h, PPS_K_RMSNORM_FWD, 0.0, norm_bytes, [&] {
+            return pps::rmsnorm_fwd(dt, xin, gamma, D.eps, T, d, rb, h->tn ? nullptr : sn, copy_in ? xb : nullptr,
+                                    h->stream);
         }));
-        // g, u = n [Wg | Wu] with h = silu(g) u in the epilogue.
+        // g, u = n [Wg | Wu] (bf16: r x [gamma Wg | gamma Wu]) with
+        // h = silu(g) u in the epilogue.
         GemmArgs a;
         a.M = T; a.N = f; a.nseg = 1;
         a.seg[0].A = sn; a.seg[0].lda = d; a.seg[0].K = d;
         a.a_kcontig = true; a.swiglu_map = true;
         if (h->tn) {
+            a.seg[0].A = xin;
             a.seg[0].B = h->wcopy + h->wgu_off[blk0 + b]; a.seg[0].ldb = d; a.b_kcontig = true;
+            a.e.rowscale = rb;
         } else {
             a.seg[0].B = wb[0]; a.seg[0].B2 = wb[1]; a.seg[0].ldb = f; a.b_kcontig = false;
         }

