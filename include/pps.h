@@ -48,6 +48,12 @@ extern "C" {
 #define PPS_ESTATE  (-5)  /* wrong state: W without split mode, W before B, twice */
 #define PPS_ENOMEM  (-6)  /* device allocation failed at create                 */
 #define PPS_EHIP    (-7)  /* a HIP runtime call or kernel launch failed         */
+#define PPS_ETOOBIG (-8)  /* pps_stage_create_noalloc: the stage needs more
+                             device memory than PPS_NOALLOC_MAX_BYTES          */
+
+/* Size of the library's fixed per-GPU device array used by
+   pps_stage_create_noalloc (64 MiB). */
+#define PPS_NOALLOC_MAX_BYTES (64ull << 20)
 
 /* ---- ops and schedule kinds ---------------------------------------------- */
 #define PPS_OP_F 0  /* forward                                              */
@@ -188,6 +194,27 @@ typedef struct pps_stage pps_stage;
  * on success.
  */
 int pps_stage_create(const pps_stage_desc* desc, pps_stage** out);
+
+/*
+ * pps_stage_create_noalloc -- pps_stage_create for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same desc, same handle, same calls
+ * afterwards; the difference is where the handle's device memory lives: its
+ * stash pool, scratch, fp32 gradients and weight copies are carved from one
+ * fixed device array of PPS_NOALLOC_MAX_BYTES that the library holds on each
+ * GPU until the process ends (looked up once per device; no hipMalloc,
+ * hipFree or other allocating call).  The gradients and the padding the
+ * kernels read are cleared with fill kernels enqueued on desc->stream; the
+ * call does not synchronize.  Host bookkeeping uses ordinary host memory.
+ * Every no-alloc handle on a GPU shares that GPU's array: only one may be in
+ * use at a time (ops of two such handles that overlap on one GPU race, and a
+ * new handle clears what the previous one left).  PPS_FLAG_PROFILE is
+ * rejected (it creates HIP events).
+ * Returns PPS_ETOOBIG if the stage needs more than PPS_NOALLOC_MAX_BYTES
+ * (pool + scratch + gradients + weight copies, each rounded up to 256
+ * bytes), otherwise what pps_stage_create returns.
+ */
+int pps_stage_create_noalloc(const pps_stage_desc* desc, pps_stage** out);
 
 /*
  * pps_stage_forward -- forward of micro-batch mb (chunk) through the stage's

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpps.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip"]
+HIP_SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "noalloc.hip"]
 HOST_SOURCES = ["schedule.cpp", "stage.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -109,6 +109,10 @@ int64_t swiglu_b_rows(int64_t ffn);
 hipError_t scale(int dtype, void* dst, const void* src, int64_t n, float scale, hipStream_t s);
 
 hipError_t fill_zero(void* p, int64_t bytes, hipStream_t s);
+
+// Device address of this device's fixed no-alloc array (PPS_NOALLOC_MAX_BYTES),
+// looked up once per device.  Returns a PPS_* status.
+int noalloc_scratch(char** out);
 hipError_t copy_bytes(void* dst, const void* src, int64_t bytes, hipStream_t s);
 
 }  // namespace pps

@@ -66,6 +66,7 @@ struct pps_stage {
 
     hipStream_t stream = nullptr;
     Layout lay;
+    bool noalloc = false;             // device memory carved from the fixed array, never freed
     char* pool = nullptr;
     char* scratch = nullptr;
     size_t scratch_bytes = 0;
@@ -217,10 +218,12 @@ void release(pps_stage* h) {
     if (!h) return;
     for (hipEvent_t e : h->ev)
         if (e) hipEventDestroy(e);
-    if (h->pool) hipFree(h->pool);
-    if (h->scratch) hipFree(h->scratch);
-    if (h->grads) hipFree(h->grads);
-    if (h->wcopy) hipFree(h->wcopy);
+    if (!h->noalloc) {
+        if (h->pool) hipFree(h->pool);
+        if (h->scratch) hipFree(h->scratch);
+        if (h->grads) hipFree(h->grads);
+        if (h->wcopy) hipFree(h->wcopy);
+    }
     delete h;
 }
 
@@ -597,10 +600,15 @@ int toy_backward_weight(pps_stage* h, int slot, int chunk) {
 // C ABI
 // ---------------------------------------------------------------------------
 
-extern "C" int pps_stage_create(const pps_stage_desc* desc, pps_stage** out) {
+namespace {
+
+// pps_stage_create and pps_stage_create_noalloc: the same handle; `noalloc`
+// takes the device memory from the library's fixed array instead of hipMalloc.
+int create_stage(const pps_stage_desc* desc, pps_stage** out, bool noalloc) {
     if (!out) return PPS_EINVAL;
     int rc = validate_desc(desc);
     if (rc != PPS_OK) return rc;
+    if (noalloc && (desc->flags & PPS_FLAG_PROFILE)) return PPS_EINVAL;
     pps_stage* h = new (std::nothrow) pps_stage();
     if (!h) return PPS_ENOMEM;
     h->d = *desc;
@@ -693,11 +701,28 @@ extern "C" int pps_stage_create(const pps_stage_desc* desc, pps_stage** out) {
     h->st.scratch_bytes = (int64_t)(h->scratch_bytes + h->wcopy_bytes);
     h->st.grad_bytes = (int64_t)h->grad_bytes;
 
+    const size_t pool_alloc = std::max<size_t>(h->lay.slot_bytes * h->S, 256);
+    const size_t grad_alloc = std::max<size_t>(h->grad_bytes, 256);
+    if (!h->bookkeeping && noalloc) {
+        const size_t need = align256(pool_alloc) + align256(h->scratch_bytes) + align256(grad_alloc) +
+                            align256(h->wcopy_bytes);
+        if (need > (size_t)PPS_NOALLOC_MAX_BYTES) { release(h); return PPS_ETOOBIG; }
+        char* base = nullptr;
+        rc = pps::noalloc_scratch(&base);
+        if (rc != PPS_OK) { release(h); return rc; }
+        h->noalloc = true;
+        size_t o = 0;
+        h->pool = base + o; o += align256(pool_alloc);
+        h->scratch = base + o; o += align256(h->scratch_bytes);
+        h->grads = reinterpret_cast<float*>(base + o); o += align256(grad_alloc);
+        h->wcopy = h->wcopy_bytes ? base + o : nullptr;
+    }
     if (!h->bookkeeping) {
-        if (hipMalloc(reinterpret_cast<void**>(&h->pool), std::max<size_t>(h->lay.slot_bytes * h->S, 256)) != hipSuccess ||
-            hipMalloc(reinterpret_cast<void**>(&h->scratch), h->scratch_bytes) != hipSuccess ||
-            hipMalloc(reinterpret_cast<void**>(&h->grads), std::max<size_t>(h->grad_bytes, 256)) != hipSuccess ||
-            (h->wcopy_bytes && hipMalloc(reinterpret_cast<void**>(&h->wcopy), h->wcopy_bytes) != hipSuccess)) {
+        if (!noalloc &&
+            (hipMalloc(reinterpret_cast<void**>(&h->pool), pool_alloc) != hipSuccess ||
+             hipMalloc(reinterpret_cast<void**>(&h->scratch), h->scratch_bytes) != hipSuccess ||
+             hipMalloc(reinterpret_cast<void**>(&h->grads), grad_alloc) != hipSuccess ||
+             (h->wcopy_bytes && hipMalloc(reinterpret_cast<void**>(&h->wcopy), h->wcopy_bytes) != hipSuccess))) {
             (void)hipGetLastError();
             release(h);
             return PPS_ENOMEM;
@@ -719,10 +744,25 @@ extern "C" int pps_stage_create(const pps_stage_desc* desc, pps_stage** out) {
             for (auto& e : h->ev)
                 if (hipEventCreate(&e) != hipSuccess) { release(h); return PPS_EHIP; }
         }
-        if (hipStreamSynchronize(h->stream) != hipSuccess) { release(h); return PPS_EHIP; }
+        if (noalloc) {
+            if (hipGetLastError() != hipSuccess) { release(h); return PPS_EHIP; }
+        } else if (hipStreamSynchronize(h->stream) != hipSuccess) {
+            release(h);
+            return PPS_EHIP;
+        }
     }
     *out = h;
     return PPS_OK;
+}
+
+}  // namespace
+
+extern "C" int pps_stage_create(const pps_stage_desc* desc, pps_stage** out) {
+    return create_stage(desc, out, false);
+}
+
+extern "C" int pps_stage_create_noalloc(const pps_stage_desc* desc, pps_stage** out) {
+    return create_stage(desc, out, true);
 }
 
 extern "C" int pps_stage_forward(pps_stage* h, int mb, int chunk, const void* x_in, void* y_out) {
@@ -916,6 +956,7 @@ extern "C" const char* pps_strerror(int s) {
         case PPS_ESTATE: return "wrong state for this call";
         case PPS_ENOMEM: return "device allocation failed";
         case PPS_EHIP: return "HIP runtime error";
+        case PPS_ETOOBIG: return "stage needs more device memory than the no-alloc array holds";
         default: return "unknown status";
     }
 }

@@ -17,7 +17,8 @@ import torch  # noqa: F401
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpps.so")
 
-OK, EINVAL, EFULL, EORDER, ENOENT, ESTATE, ENOMEM, EHIP = 0, -1, -2, -3, -4, -5, -6, -7
+OK, EINVAL, EFULL, EORDER, ENOENT, ESTATE, ENOMEM, EHIP, ETOOBIG = 0, -1, -2, -3, -4, -5, -6, -7, -8
+NOALLOC_MAX_BYTES = 64 << 20
 OP_F, OP_B, OP_W = 0, 1, 2
 GPIPE, ONE_F_ONE_B, ZB1P, ZB2P = 0, 1, 2, 3
 BLOCK_SWIGLU, BLOCK_TOY_GELU = 0, 1
@@ -29,7 +30,7 @@ DTYPE_BY_NAME = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}
 BLOCK_BY_NAME = {"swiglu": BLOCK_SWIGLU, "toy": BLOCK_TOY_GELU}
 
 EXPORTED = [
-    "pps_make_schedule", "pps_stage_create", "pps_stage_forward", "pps_stage_backward",
+    "pps_make_schedule", "pps_stage_create", "pps_stage_create_noalloc", "pps_stage_forward", "pps_stage_backward",
     "pps_stage_backward_weight", "pps_stage_zero_grad", "pps_stage_get_grad", "pps_stage_sync",
     "pps_stage_get_stats", "pps_stage_get_oplog", "pps_stage_kernel_times", "pps_kernel_name",
     "pps_stage_destroy", "pps_strerror", "pps_scale", "pps_simulate_pipeline",
@@ -87,6 +88,7 @@ def lib():
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
         L.pps_make_schedule.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(PpsOp), i32, ctypes.POINTER(i32)]
         L.pps_stage_create.argtypes = [ctypes.POINTER(PpsStageDesc), ctypes.POINTER(vp)]
+        L.pps_stage_create_noalloc.argtypes = [ctypes.POINTER(PpsStageDesc), ctypes.POINTER(vp)]
         L.pps_stage_forward.argtypes = [vp, i32, i32, vp, vp]
         L.pps_stage_backward.argtypes = [vp, i32, i32, vp, vp]
         L.pps_stage_backward_weight.argtypes = [vp, i32, i32]
@@ -164,7 +166,8 @@ class Stage:
     """One pipeline stage handle (pps_stage)."""
 
     def __init__(self, P, M, k, v=1, kind=ONE_F_ONE_B, block=BLOCK_SWIGLU, dtype=DTYPE_BF16, L=1,
-                 d=64, ffn=64, T=8, eps=1e-6, weights=None, stream=None, flags=0, profile_capacity=0):
+                 d=64, ffn=64, T=8, eps=1e-6, weights=None, stream=None, flags=0, profile_capacity=0,
+                 noalloc=False):
         self._h = None
         nw = 4 if block == BLOCK_SWIGLU else 2
         desc = PpsStageDesc()
@@ -183,7 +186,8 @@ class Stage:
         else:
             desc.weights = None
         h = ctypes.c_void_p()
-        _check(lib().pps_stage_create(ctypes.byref(desc), ctypes.byref(h)), "pps_stage_create")
+        fn = "pps_stage_create_noalloc" if noalloc else "pps_stage_create"
+        _check(getattr(lib(), fn)(ctypes.byref(desc), ctypes.byref(h)), fn)
         self._h = h
         self.desc = desc
 
@@ -277,9 +281,10 @@ def _hip():
 
 
 def stage_from_config(cfg, weights=None, stream=None, flags=0, profile_capacity=0, k=None, T=None, M=None,
-                      kind=None):
+                      kind=None, noalloc=False):
     """Stage handle for a ``configs.StageConfig`` (optionally overriding k, T, M, kind)."""
     return Stage(P=cfg.P, M=cfg.M if M is None else M, k=cfg.k if k is None else k, v=cfg.v,
                  kind=KIND_BY_NAME[cfg.kind if kind is None else kind], block=BLOCK_BY_NAME[cfg.block],
                  dtype=DTYPE_BY_NAME[cfg.dtype], L=cfg.L, d=cfg.d, ffn=cfg.f, T=cfg.T if T is None else T,
-                 eps=cfg.eps, weights=weights, stream=stream, flags=flags, profile_capacity=profile_capacity)
+                 eps=cfg.eps, weights=weights, stream=stream, flags=flags, profile_capacity=profile_capacity,
+                 noalloc=noalloc)

@@ -301,3 +301,30 @@ def test_simulate_pipeline_errors():
                  (4, 6, 1, 9, 1.0, 1.0, 0.0), (4, 6, 1, pps.ONE_F_ONE_B, 1.0, float("inf"), 0.0)]:
         assert L.pps_simulate_pipeline(*args, ctypes.byref(mk), ctypes.byref(bu)) == pps.EINVAL, args
     assert L.pps_simulate_pipeline(4, 6, 1, pps.ONE_F_ONE_B, 1.0, 1.0, 0.0, None, ctypes.byref(bu)) == pps.EINVAL
+
+
+def test_noalloc_create_rejects_before_touching_the_device():
+    # The size check and the flag check come before any HIP call, so they run
+    # without a GPU: a stage larger than the fixed array is PPS_ETOOBIG, and
+    # PPS_FLAG_PROFILE (which creates HIP events) is PPS_EINVAL.
+    L = _lib_or_skip()
+    fake = (ctypes.c_void_p * 64)(*([0x1000] * 64))
+
+    def desc(**over):
+        d = pps.PpsStageDesc()
+        base = dict(P=4, M=8, k=0, v=1, kind=pps.ONE_F_ONE_B, block_type=pps.BLOCK_SWIGLU, dtype=pps.DTYPE_BF16,
+                    L=2, d=1024, ffn=2816, T=2048)
+        for key, val in {**base, **over}.items():
+            setattr(d, key, val)
+        d.eps = 1e-6
+        d.weights = ctypes.cast(fake, ctypes.POINTER(ctypes.c_void_p))
+        return d
+
+    h = ctypes.c_void_p()
+    big = desc()   # 4 stash entries of ~55 MB alone exceed 64 MiB
+    assert L.pps_stage_create_noalloc(ctypes.byref(big), ctypes.byref(h)) == pps.ETOOBIG
+    assert not h.value
+    prof = desc(d=64, ffn=64, T=8, flags=pps.FLAG_PROFILE, profile_capacity=16)
+    assert L.pps_stage_create_noalloc(ctypes.byref(prof), ctypes.byref(h)) == pps.EINVAL
+    assert not h.value
+    assert "no-alloc" in pps.strerror(pps.ETOOBIG)
