@@ -36,10 +36,10 @@ PEAK_HBM_GBS = 8000.0
 # copy kernel measured in the same runs).  Valid only for the GEMM source they were taken on.
 TRAFFIC = {
     "config": "c3_80layer_p8_stage0",
-    "gemm_source_sha1": "85c199bcd48b2dc210598ec386bee64d38d871b3",
+    "gemm_source_sha1": "828caa5a13b7543d069455a141e85f1090ecaabd",
     "bytes_per_launch": {
-        "gemm_gateup_swiglu": 13.37e9, "gemm_down_residual": 5.98e9, "gemm_dh_swiglu_bwd": 8.84e9,
-        "gemm_dn": 12.27e9, "gemm_wgrad_down": 8.291e9, "gemm_wgrad_gateup": 8.291e9,
+        "gemm_gateup_swiglu": 13.775e9, "gemm_down_residual": 6.012e9, "gemm_dh_swiglu_bwd": 8.653e9,
+        "gemm_dn": 12.583e9, "gemm_wgrad_down": 8.654e9, "gemm_wgrad_gateup": 8.654e9,
     },
 }
 
@@ -107,6 +107,54 @@ def cpu_baseline(cfg, params_dev, budget_s=20.0):
     }
 
 
+def vendor_reference(cfg, reps=10):
+    """hipBLASLt (through torch.mm / torch.addmm) on the stage's six GEMM shapes, both operands
+    K-contiguous as the stage's own kernel reads them: plain bf16 products with nothing fused, and
+    the weight-gradient shapes also as fp32 C += A B.  A comparison point for the stage's fused
+    kernels, not part of the stage."""
+    import torch
+    T, d, f = cfg.T, cfg.d, cfg.f
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed + 7)
+    # small check that addmm with an fp32 out_dtype really computes C + A B
+    a = torch.randn(256, 512, generator=gen, device=dev).to(torch.bfloat16)
+    b = torch.randn(384, 512, generator=gen, device=dev).to(torch.bfloat16)
+    c = torch.randn(256, 384, generator=gen, device=dev)
+    got = torch.addmm(c, a, b.t(), out_dtype=torch.float32)
+    want = c + a.float() @ b.float().t()
+    check = float((got - want).norm() / want.norm())
+    shapes = [("gemm_gateup", T, 2 * f, d, False), ("gemm_down", T, d, f, False), ("gemm_dh", T, f, d, False),
+              ("gemm_dn", T, d, 2 * f, False), ("gemm_wgrad_down", f, d, T, True), ("gemm_wgrad_gateup", d, 2 * f, T, True)]
+    out = {}
+    for name, M, N, K, acc in shapes:
+        a = torch.randn(M, K, generator=gen, device=dev).to(torch.bfloat16)
+        b = (0.02 * torch.randn(N, K, generator=gen, device=dev)).to(torch.bfloat16)
+        fl = 2.0 * M * N * K
+        runs = [("bf16_out", lambda: torch.mm(a, b.t()))]
+        if acc:
+            c = torch.zeros(M, N, device=dev)
+            runs.append(("fp32_accumulate", lambda: torch.addmm(c, a, b.t(), out_dtype=torch.float32, out=c)))
+        for kind, fn in runs:
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            e1.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            out[f"{name}.{kind}"] = {"M": M, "N": N, "K": K, "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)}
+            _log(f"vendor {name} {kind}: {ms:.3f} ms, {fl / ms / 1e9:.1f} TFLOP/s")
+        del a, b
+        torch.cuda.empty_cache()
+    return {"library": "hipBLASLt via torch.mm / torch.addmm(out_dtype=float32)", "reps": reps,
+            "addmm_fp32_check_rel_l2": check, "gemms": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +169,9 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain fp32 copy kernel (pps_scale by 1.0) three times over this many MiB: "
                          "a reference of known size for the HBM byte counters")
+    ap.add_argument("--vendor-reference", action="store_true",
+                    help="instead of the stage pass, time hipBLASLt on the workload's six GEMM shapes "
+                         "(plain bf16 products; fp32 accumulate for the weight gradients) and print them as JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one pipeline stage on one GPU; --gpus {args.gpus} is not supported "
@@ -136,6 +187,13 @@ def main():
     cfg = PRESETS[args.config]
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    if args.vendor_reference:
+        if cfg.block != "swiglu":
+            sys.exit("--vendor-reference needs a SwiGLU workload")
+        res = vendor_reference(cfg)
+        res["workload"] = cfg.name
+        print(json.dumps(res), flush=True)
+        return
     stream = torch.cuda.current_stream()
     dtype_id = pps.DTYPE_BY_NAME[cfg.dtype]
     kind_id = pps.KIND_BY_NAME[cfg.kind]
