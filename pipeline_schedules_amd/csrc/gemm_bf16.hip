@@ -183,17 +183,34 @@ __device__ __forceinline__ void epi8(const EpiPtr& a, const float (&w)[8], const
     }
 }
 
-// SwiGLU backward for 8 columns: stores dg, du and returns h = silu(g) u (as
-// the forward computed it) for the caller to store transposed.
+// SwiGLU backward for 8 columns: stores dg, du and returns them with
+// h = silu(g) u (from the stored g, u) packed to bf16, for the caller to
+// store transposed.
 __device__ __forceinline__ void epi8_swiglu_bwd(const EpiPtr& a, const float (&w)[8], const EpiIn8<EPI_SWIGLU_BWD>& in,
-                                                float (&hh)[8]) {
-    float g[8], u[8], dg[8], du[8];
+                                                uint4& ph, uint4& pdg, uint4& pdu) {
+    float g[8], u[8], dg[8], du[8], hh[8];
     unpack8(in.g, g);
     unpack8(in.u, u);
 #pragma unroll
     for (int k = 0; k < 8; ++k) swiglu_h_bwd_f(w[k], g[k], u[k], hh[k], dg[k], du[k]);
-    *reinterpret_cast<uint4*>(a.o0) = pack8(dg);
-    *reinterpret_cast<uint4*>(a.o1) = pack8(du);
+    ph = pack8(hh);
+    pdg = pack8(dg);
+    pdu = pack8(du);
+    *reinterpret_cast<uint4*>(a.o0) = pdg;
+    *reinterpret_cast<uint4*>(a.o1) = pdu;
+}
+
+__device__ __forceinline__ uint32_t u4_at(const uint4& v, int c) { return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w; }
+
+// Transposed outputs of the SwiGLU backward (h, dg, du) go through LDS, 24 KB
+// per wavefront: per output a [128 columns][32 rows] bf16 block, 64 bytes per
+// column.  Column c sits in slot c ^ ((c >> 3) & 1) and its 16-byte row piece
+// p at position p ^ ((c >> 4) & 3), so the 8-byte writes (4 rows of one
+// column per lane) and the 16-byte reads (8 rows) spread over all banks.
+constexpr int TSTAGE = 24576;
+__device__ __forceinline__ int tstage_off(int o, int col, int q8) {   // q8: 8-byte chunk 0..7
+    const int slot = col ^ ((col >> 3) & 1);
+    return o * 8192 + slot * 64 + (((q8 >> 1) ^ ((col >> 4) & 3)) << 4) + ((q8 & 1) << 3);
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt left at its maximum).
@@ -504,14 +521,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             if (i + NB - 1 < 8) prefetch(i + NB - 1, in[(i + NB - 1) % NB]);
-            float hh[4][8];   // SwiGLU backward: h of this row group
+            uint4 pk[3][4];   // SwiGLU backward: h, dg, du of this row group, bf16
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 if constexpr (EPI == EPI_SWIGLU_BWD) {
                     float w[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) w[j] = acc[i][j][r];
-                    if (ok(i, r)) epi8_swiglu_bwd(ptr(i, r), w, in[i % NB][r], hh[r]);
+                    if (ok(i, r)) epi8_swiglu_bwd(ptr(i, r), w, in[i % NB][r], pk[0][r], pk[1][r], pk[2][r]);
                 } else if constexpr (EPI == EPI_SWIGLU) {
                     const float sc = rsc[i][r];
                     const float g[4] = {acc[i][0][r] * sc, acc[i][1][r] * sc, acc[i][2][r] * sc, acc[i][3][r] * sc};
@@ -525,18 +542,54 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
                 }
             }
             if constexpr (EPI == EPI_SWIGLU_BWD && FAST) {
-                // h = silu(g) u (as the forward computed it) for the weight
-                // gradient, written transposed: column j's four rows of this
-                // row group are 8 consecutive bytes of hT row n0 + lc + j
-                // (only full tiles: the dispatcher requires them with out2)
+                // h (and, with out3, dg and du) for the weight gradients,
+                // written transposed (T-contiguous) through LDS: column j's
+                // four rows of this row group are one 8-byte chunk of the
+                // wavefront's staging block; after two row groups, 32 rows
+                // of each column go out as 16-byte pieces.  Only full tiles:
+                // the dispatcher requires them with out2.
                 if (e.out2) {
-                    const int64_t row0 = m0 + lr + i * 16;
+                    const int nout = e.out3 ? 3 : 1;
+                    char* const wst = smem + wave_s * TSTAGE;
+                    const int q8 = 4 * (i & 1) + (lane >> 4);
+                    const int lcl = 8 * (lane & 15);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int64_t col = n0 + lc + j;
-                        const float v[4] = {hh[0][j], hh[1][j], hh[2][j], hh[3][j]};
-                        uint2* o = reinterpret_cast<uint2*>(static_cast<char*>(e.out2) + (col * e.ld2 + row0) * 2);
-                        *o = pack4(v);
+                    for (int o = 0; o < 3; ++o) {
+                        if (o < nout) {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) {
+                                const int c = j >> 1, sh = (j & 1) * 16;
+                                const uint32_t r0 = (u4_at(pk[o][0], c) >> sh) & 0xffffu, r1 = (u4_at(pk[o][1], c) >> sh) & 0xffffu;
+                                const uint32_t r2 = (u4_at(pk[o][2], c) >> sh) & 0xffffu, r3 = (u4_at(pk[o][3], c) >> sh) & 0xffffu;
+                                *reinterpret_cast<uint2*>(wst + tstage_off(o, lcl + j, q8)) = make_uint2(r0 | (r1 << 16), r2 | (r3 << 16));
+                            }
+                        }
+                    }
+                    if (i & 1) {
+                        // the wavefront's own staging writes are visible to its reads
+                        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                        __builtin_amdgcn_wave_barrier();
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                        const int pq = lane & 3;
+                        const int64_t trow = m0 + wm * 128 + 32 * (i >> 1) + 8 * pq;   // first of 8 rows
+#pragma unroll
+                        for (int o = 0; o < 3; ++o) {
+                            if (o < nout) {
+                                char* const dst = o == 0 ? static_cast<char*>(e.out2)
+                                                : o == 1 ? static_cast<char*>(e.out3)
+                                                         : static_cast<char*>(e.out3) + e.nsplit * e.ld2 * 2;
+#pragma unroll
+                                for (int k = 0; k < 8; ++k) {
+                                    const int col = 16 * k + (lane >> 2);
+                                    const uint4 v = *reinterpret_cast<const uint4*>(wst + tstage_off(o, col, 2 * pq));
+                                    *reinterpret_cast<uint4*>(dst + ((n0 + wn * 128 + col) * e.ld2 + trow) * 2) = v;
+                                }
+                            }
+                        }
+                        // reads done before the next pair overwrites the block
+                        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                        __builtin_amdgcn_wave_barrier();
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                     }
                 }
             }
@@ -578,11 +631,13 @@ hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
     if (a.N % 8 || a.e.ld0 % 8 || (in && a.e.ldi0 % 8) || (a.epi == EPI_SWIGLU_BWD && a.e.nsplit % 8))
         return hipErrorInvalidValue;
     if (a.epi == EPI_ACC_F32 && a.e.nsplit < a.N) return hipErrorInvalidValue;
-    if (a.epi == EPI_SWIGLU_BWD && a.e.out2 && (a.M % BM || a.N % BN || a.e.ld2 < a.M || a.e.ld2 % 4))
-        return hipErrorInvalidValue;   // h is written transposed from full tiles only
+    if (a.epi == EPI_SWIGLU_BWD && a.e.out2 && (a.M % BM || a.N % BN || a.e.ld2 < a.M || a.e.ld2 % 8))
+        return hipErrorInvalidValue;   // h (dg, du) are written transposed from full tiles only
+    if (a.e.out3 && (a.epi != EPI_SWIGLU_BWD || !a.e.out2)) return hipErrorInvalidValue;
     const uintptr_t ptrs = reinterpret_cast<uintptr_t>(a.e.out0) | reinterpret_cast<uintptr_t>(a.e.out1) |
                            reinterpret_cast<uintptr_t>(a.e.out2) | reinterpret_cast<uintptr_t>(a.e.in0) |
-                           reinterpret_cast<uintptr_t>(a.e.in1) | reinterpret_cast<uintptr_t>(a.e.rowscale);
+                           reinterpret_cast<uintptr_t>(a.e.in1) | reinterpret_cast<uintptr_t>(a.e.rowscale) |
+                           reinterpret_cast<uintptr_t>(a.e.out3);
     if (ptrs % 16) return hipErrorInvalidValue;
     Params p{};
     p.M = a.M;

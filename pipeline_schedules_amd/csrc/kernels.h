@@ -22,7 +22,7 @@ enum Epi {
                          // bf16 GEMM: g, u = rowscale[m] * acc first, h from the unrounded g, u
     EPI_SWIGLU_BWD = 3,  // dh=acc; g=in0,u=in1 (ldi0) -> out0[m*ld0+n]=dg, out0[..+nsplit]=du,
                          // and if out2: h = silu(g) u at out2[m*ldi0+n] (fp32 GEMM) or
-                         // out2[n*ld2+m] (bf16 GEMM)
+                         // out2[n*ld2+m] (bf16 GEMM; with out3 also dg, du transposed)
     EPI_ACC_F32 = 4,     // n <  nsplit: out0[m*ld0+n] += acc; else out1[m*ld1+n-nsplit] += acc
                          // (bf16: out0 only, nsplit >= N)
     EPI_BIAS_GELU = 5,   // z = acc + bias[n]; out0 = z, out1 = GELU(z)   (fp32 only)
@@ -40,8 +40,10 @@ struct EpiArgs {
     int64_t nsplit = 0;
     const float* bias = nullptr;
     int64_t ld2 = 0;   // SwiGLU backward, bf16 GEMM: h is written transposed, out2[n*ld2 + m]
-                       // (needs M and N multiples of 256, ld2 % 4 == 0)
+                       // (needs M and N multiples of 256, ld2 % 8 == 0)
     const float* rowscale = nullptr;   // SwiGLU, bf16 GEMM: per output row factor (RMSNorm r)
+    void* out3 = nullptr;   // SwiGLU backward, bf16 GEMM, with out2: dg and du also written
+                            // transposed, out3[n*ld2 + m] and out3[(nsplit + n)*ld2 + m]
 };
 
 struct GemmSeg {

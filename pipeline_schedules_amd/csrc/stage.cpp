@@ -75,7 +75,7 @@ struct pps_stage {
     bool ac = false;
     size_t s_rc = 0;
     size_t s_n = 0, s_h = 0, s_dgu = 0, s_dn = 0, s_dxa = 0, s_dxb = 0, s_part = 0, s_dz = 0;
-    // bf16 weight gradients: T-contiguous copies of h, n, dy and dg|du
+    // bf16 weight gradients: T-contiguous h, n, dy and dg|du (copies, or from the dh epilogue)
     // ([features, Tp], Tp = T rounded up to 8, zero-padded)
     size_t s_hT = 0, s_nT = 0, s_dyT = 0, s_dguT = 0;
     int64_t Tp = 0;
@@ -349,10 +349,10 @@ int swiglu_forward(pps_stage* h, int slot, int chunk, const void* x_in, void* y_
 // The GEMMs reduce over the T rows.  bf16: the operands are first copied
 // T-contiguous ([features, T]) for the K-contiguous kernel; fp32 reads them as
 // stored.  With `have_nh` the backward just produced n (scratch) and h
-// (bf16: already T-contiguous, written so by the dh epilogue; fp32: scratch);
-// otherwise both are recomputed from the stash.
-// bf16 without the split: the dh epilogue writes hT (T and ffn multiples of
-// the 256 x 256 GEMM tile)
+// (bf16: h and dg|du already T-contiguous, written so by the dh epilogue;
+// fp32: scratch); otherwise n and h are recomputed from the stash.
+// bf16 without the split: the dh epilogue writes hT and dguT (T and ffn
+// multiples of the 256 x 256 GEMM tile)
 bool hT_fused(const pps_stage* h) { return h->tn && h->d.T % 256 == 0 && h->d.ffn % 256 == 0; }
 
 int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, const void* dgu, bool have_nh) {
@@ -393,10 +393,11 @@ int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, cons
                 return pps::transpose_bf16(src, T, cols, cols, dst, Tp, 0, 0, h->stream);
             });
         };
+        // with have_nh the dh epilogue wrote hT and dguT (full tiles)
         if (!have_nh) PPS_TRY(tr(sh, f, hT));
         PPS_TRY(tr(dy, d, dyT));
         PPS_TRY(tr(sn, d, nT));
-        PPS_TRY(tr(dgu, 2 * f, dguT));
+        if (!have_nh) PPS_TRY(tr(dgu, 2 * f, dguT));
         a.seg[0].A = hT; a.seg[0].lda = Tp; a.seg[0].B = dyT; a.seg[0].ldb = Tp;
         c.seg[0].A = nT; c.seg[0].lda = Tp; c.seg[0].B = dguT; c.seg[0].ldb = Tp;
         a.a_kcontig = a.b_kcontig = c.a_kcontig = c.b_kcontig = true;
@@ -469,9 +470,12 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
         a.e.in0 = ab + h->lay.g[b]; a.e.in1 = ab + h->lay.u[b]; a.e.ldi0 = f;
         a.e.out0 = dgu; a.e.ld0 = 2 * f; a.e.nsplit = f; a.e.out2 = sh;
         if (h->tn && sh) {
-            // the weight gradient reads h T-contiguous: the epilogue writes it
-            // so when its tiles are full; otherwise h and n are recomputed at dW
-            a.e.out2 = hT_fused(h) ? h->scratch + h->s_hT : nullptr;
+            // the weight gradients read h and dg|du T-contiguous: the epilogue
+            // writes them so when its tiles are full; otherwise h and n are
+            // recomputed at dW and h, dg|du copied
+            const bool fused = hT_fused(h);
+            a.e.out2 = fused ? h->scratch + h->s_hT : nullptr;
+            a.e.out3 = fused ? h->scratch + h->s_dguT : nullptr;
             a.e.ld2 = h->Tp;
         }
         PPS_TRY(timed(h, PPS_K_DH, gemm_flops(T, f, d), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
