@@ -292,10 +292,10 @@ int pps_stage_get_oplog(const pps_stage* h, pps_op* ops, int cap, int* n);
 #define PPS_K_DN            4  /* dn = dg Wg^T + du Wu^T                         */
 #define PPS_K_RMSNORM_BWD   5  /* dx = dy + r a - r^3 x (a.x)/d; dgamma partials; n */
 #define PPS_K_DGAMMA        6  /* dgamma += sum of partials                      */
-#define PPS_K_PREP_W        7  /* n = x r gamma, h = silu(g) u again at W: split, or bf16 with T or ffn not multiples of 256 */
+#define PPS_K_PREP_W        7  /* n = x r gamma, h = silu(g) u again at W (fp32 split; bf16 makes them T-contiguous in the copies) */
 #define PPS_K_WGRAD_DOWN    8  /* dWd += h^T dy                                  */
 #define PPS_K_WGRAD_GATEUP  9  /* dWg += n^T dg, dWu += n^T du                   */
-#define PPS_K_COPY         10  /* copies: into the stash; per-pass weight copies; T-contiguous n, dy (and h, dg|du where the dh epilogue does not write them) for bf16 dW */
+#define PPS_K_COPY         10  /* copies: into the stash; per-pass weight copies; T-contiguous n (from x r gamma), dy (and h from g, u, dg|du where the dh epilogue does not write them) for bf16 dW */
 #define PPS_K_TOY_FWD      11  /* z = x W + b; y = GELU(z)                       */
 #define PPS_K_TOY_DZ       12  /* dz = dy GELU'(z)                               */
 #define PPS_K_TOY_DX       13  /* dx = dz W^T                                    */

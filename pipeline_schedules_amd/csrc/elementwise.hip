@@ -235,10 +235,15 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ a
 // columns c < cols (cols % 8 == 0); destination row map(c), column r, stride
 // ldd (ldd % 8 == 0); destination columns in [rows, ldd) are written as zero.
 // map(c) = c, or with grp > 0: (c / grp) * 2 grp + half * grp + c % grp
-// (gate/up interleave of the forward weight copy).
+// (gate/up interleave of the forward weight copy).  The value moved is
+// src[r, c] (x rowscale[r], then x colscale[c]: the RMSNorm output (x r) gamma
+// as the forward computed it), or with src2 silu(src[r, c]) src2[r, c] (h from
+// g and u, the expression the SwiGLU epilogues use).
 __global__ __launch_bounds__(256) void tile_transpose_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
                                                              int64_t lds, uint16_t* __restrict__ dst, int64_t ldd,
-                                                             int grp, int half, const float* __restrict__ rowscale) {
+                                                             int grp, int half, const float* __restrict__ rowscale,
+                                                             const float* __restrict__ colscale,
+                                                             const uint16_t* __restrict__ src2) {
     __shared__ float tile[64][65];
     const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
     const int t = threadIdx.x;
@@ -249,10 +254,20 @@ __global__ __launch_bounds__(256) void tile_transpose_kernel(const uint16_t* __r
         float v[8];
         if (row < rows && col < cols) {
             Vec8<uint16_t>::load(src + row * lds + col, v);
+            if (src2) {
+                float w[8];
+                Vec8<uint16_t>::load(src2 + row * lds + col, w);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = swiglu_f(v[j], w[j]);
+            }
             if (rowscale) {
                 const float sc = rowscale[row];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) v[j] *= sc;   // rounded to bf16 by the store
+            }
+            if (colscale) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] *= colscale[col + j];
             }
         } else {
 #pragma unroll
@@ -389,12 +404,13 @@ hipError_t colsum_acc(const float* a, int64_t T, int64_t d, float* out, hipStrea
 }
 
 hipError_t transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t lds, void* dst, int64_t ldd, int grp,
-                          int half, hipStream_t s, const float* rowscale) {
+                          int half, hipStream_t s, const float* rowscale, const float* colscale, const void* src2) {
     if (cols <= 0 || ldd <= 0) return hipSuccess;
     if (cols % 8 || ldd % 8 || lds % 8) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((ldd + 63) / 64), (unsigned)((cols + 63) / 64));
     hipLaunchKernelGGL(tile_transpose_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), rows, cols, lds,
-                       static_cast<uint16_t*>(dst), ldd, grp, half, rowscale);
+                       static_cast<uint16_t*>(dst), ldd, grp, half, rowscale, colscale,
+                       static_cast<const uint16_t*>(src2));
     return hipGetLastError();
 }
 

@@ -542,20 +542,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
                 }
             }
             if constexpr (EPI == EPI_SWIGLU_BWD && FAST) {
-                // h (and, with out3, dg and du) for the weight gradients,
+                // h (out2) and dg, du (out3) for the weight gradients,
                 // written transposed (T-contiguous) through LDS: column j's
                 // four rows of this row group are one 8-byte chunk of the
                 // wavefront's staging block; after two row groups, 32 rows
                 // of each column go out as 16-byte pieces.  Only full tiles:
                 // the dispatcher requires them with out2.
-                if (e.out2) {
-                    const int nout = e.out3 ? 3 : 1;
+                if (e.out2 || e.out3) {
+                    const int olo = e.out2 ? 0 : 1, ohi = e.out3 ? 3 : 1;   // outputs olo .. ohi-1
                     char* const wst = smem + wave_s * TSTAGE;
                     const int q8 = 4 * (i & 1) + (lane >> 4);
                     const int lcl = 8 * (lane & 15);
 #pragma unroll
                     for (int o = 0; o < 3; ++o) {
-                        if (o < nout) {
+                        if (o >= olo && o < ohi) {
 #pragma unroll
                             for (int j = 0; j < 8; ++j) {
                                 const int c = j >> 1, sh = (j & 1) * 16;
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
                         const int64_t trow = m0 + wm * 128 + 32 * (i >> 1) + 8 * pq;   // first of 8 rows
 #pragma unroll
                         for (int o = 0; o < 3; ++o) {
-                            if (o < nout) {
+                            if (o >= olo && o < ohi) {
                                 char* const dst = o == 0 ? static_cast<char*>(e.out2)
                                                 : o == 1 ? static_cast<char*>(e.out3)
                                                          : static_cast<char*>(e.out3) + e.nsplit * e.ld2 * 2;
@@ -631,9 +631,9 @@ hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
     if (a.N % 8 || a.e.ld0 % 8 || (in && a.e.ldi0 % 8) || (a.epi == EPI_SWIGLU_BWD && a.e.nsplit % 8))
         return hipErrorInvalidValue;
     if (a.epi == EPI_ACC_F32 && a.e.nsplit < a.N) return hipErrorInvalidValue;
-    if (a.epi == EPI_SWIGLU_BWD && a.e.out2 && (a.M % BM || a.N % BN || a.e.ld2 < a.M || a.e.ld2 % 8))
-        return hipErrorInvalidValue;   // h (dg, du) are written transposed from full tiles only
-    if (a.e.out3 && (a.epi != EPI_SWIGLU_BWD || !a.e.out2)) return hipErrorInvalidValue;
+    if (a.epi == EPI_SWIGLU_BWD && (a.e.out2 || a.e.out3) && (a.M % BM || a.N % BN || a.e.ld2 < a.M || a.e.ld2 % 8))
+        return hipErrorInvalidValue;   // h, dg, du are written transposed from full tiles only
+    if (a.e.out3 && a.epi != EPI_SWIGLU_BWD) return hipErrorInvalidValue;
     const uintptr_t ptrs = reinterpret_cast<uintptr_t>(a.e.out0) | reinterpret_cast<uintptr_t>(a.e.out1) |
                            reinterpret_cast<uintptr_t>(a.e.out2) | reinterpret_cast<uintptr_t>(a.e.in0) |
                            reinterpret_cast<uintptr_t>(a.e.in1) | reinterpret_cast<uintptr_t>(a.e.rowscale) |

@@ -42,8 +42,8 @@ struct EpiArgs {
     int64_t ld2 = 0;   // SwiGLU backward, bf16 GEMM: h is written transposed, out2[n*ld2 + m]
                        // (needs M and N multiples of 256, ld2 % 8 == 0)
     const float* rowscale = nullptr;   // SwiGLU, bf16 GEMM: per output row factor (RMSNorm r)
-    void* out3 = nullptr;   // SwiGLU backward, bf16 GEMM, with out2: dg and du also written
-                            // transposed, out3[n*ld2 + m] and out3[(nsplit + n)*ld2 + m]
+    void* out3 = nullptr;   // SwiGLU backward, bf16 GEMM: dg and du also written transposed,
+                            // out3[n*ld2 + m] and out3[(nsplit + n)*ld2 + m] (full tiles, as out2)
 };
 
 struct GemmSeg {
@@ -97,12 +97,15 @@ hipError_t gelu_bwd(const float* dy, const float* z, int64_t count, float* dz, h
 // out[j] += sum_t a[t, j]  (fp32, fixed order)
 hipError_t colsum_acc(const float* a, int64_t T, int64_t d, float* out, hipStream_t s);
 
-// Tiled bf16 transpose: dst[map(c), r] = src[r, c] (times rowscale[r] when
-// given, rounded to bf16) for r < rows, c < cols; dst columns in [rows, ldd)
-// are zeroed.  map(c) = c, or (c/grp)*2grp + half*grp + c%grp with grp > 0.
-// cols, lds and ldd must be multiples of 8.
+// Tiled bf16 transpose: dst[map(c), r] = v(r, c) rounded to bf16, for
+// r < rows, c < cols; dst columns in [rows, ldd) are zeroed.  v = src[r, c],
+// times rowscale[r] and then colscale[c] when given; with src2 (same layout
+// as src) v = silu(src[r, c]) src2[r, c] instead (h from g and u).
+// map(c) = c, or (c/grp)*2grp + half*grp + c%grp with grp > 0.  cols, lds and
+// ldd must be multiples of 8.
 hipError_t transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t lds, void* dst, int64_t ldd, int grp,
-                          int half, hipStream_t s, const float* rowscale = nullptr);
+                          int half, hipStream_t s, const float* rowscale = nullptr, const float* colscale = nullptr,
+                          const void* src2 = nullptr);
 
 // Rows of the interleaved gate/up weight copy used by the forward GEMM.
 int64_t swiglu_b_rows(int64_t ffn);

@@ -16,7 +16,8 @@
 // SwiGLU block b of an entry keeps x [T,d], r [T] (fp32), g and u [T,ffn].
 // With the Zero-Bubble split ([GPipe->ZB Zero Bubble]: B = dX now, W = dW
 // later, X and G stay resident until W) the entry also keeps dg|du [T,2ffn]
-// and dy [T,d] per block after B, until W.
+// (bf16 on full 256-row tiles: T-contiguous, [2ffn,T]) and dy [T,d] per
+// block after B, until W.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -144,7 +145,8 @@ hipError_t timed(pps_stage* h, int kernel, double flops, double bytes, F&& launc
         }                                      \
     } while (0)
 
-// With the split, each block also keeps dg|du [T, 2 ffn] and dy [T, d] for
+// With the split, each block also keeps dg|du [T, 2 ffn] (or, T-contiguous,
+// [2 ffn, T]: same bytes, T being a multiple of 256 then) and dy [T, d] for
 // the deferred weight-gradient GEMMs.
 Layout make_layout(const pps_stage_desc& d, bool swiglu, bool split, int es) {
     Layout L;
@@ -368,9 +370,9 @@ int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, cons
     char* ab = acts(h, slot);
     char* sn = h->scratch + h->s_n;
     char* sh = h->scratch + h->s_h;
-    if (!have_nh) {
-        const char* xb = act_x(h, slot, b);
-        const float* rb = reinterpret_cast<const float*>(ab + h->lay.r[b]);
+    const char* xb = act_x(h, slot, b);
+    const float* rb = reinterpret_cast<const float*>(ab + h->lay.r[b]);
+    if (!have_nh && !h->tn) {
         PPS_TRY(timed(h, PPS_K_PREP_W, 0.0, (double)T * (2.0 * d + 3.0 * f) * es + T * 4.0 + d * 4.0, [&] {
             return pps::prep_w(dt, xb, rb, gamma, ab + h->lay.g[b], ab + h->lay.u[b], T, d, f, sn, sh, h->stream);
         }));
@@ -388,18 +390,23 @@ int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, cons
         char* nT = h->scratch + h->s_nT;
         char* dyT = h->scratch + h->s_dyT;
         char* dguT = h->scratch + h->s_dguT;
-        auto tr = [&](const void* src, int64_t cols, void* dst) {
-            return timed(h, PPS_K_COPY, 0.0, 2.0 * T * cols * 2, [&] {
-                return pps::transpose_bf16(src, T, cols, cols, dst, Tp, 0, 0, h->stream);
+        auto tr = [&](const void* src, int64_t cols, void* dst, const float* rs = nullptr, const float* cs = nullptr,
+                      const void* src2 = nullptr) {
+            return timed(h, PPS_K_COPY, 0.0, (src2 ? 3.0 : 2.0) * T * cols * 2, [&] {
+                return pps::transpose_bf16(src, T, cols, cols, dst, Tp, 0, 0, h->stream, rs, cs, src2);
             });
         };
-        // with have_nh the dh epilogue wrote hT and dguT (full tiles)
-        if (!have_nh) PPS_TRY(tr(sh, f, hT));
+        // n = (x r) gamma and (unless the dh epilogue wrote them: have_nh)
+        // h = silu(g) u come T-contiguous straight from the stash; dg|du
+        // likewise from the dh epilogue, from the entry (split, full tiles)
+        // or by a copy
+        const bool entry_dguT = h->split && hT_fused(h);
+        PPS_TRY(tr(xb, d, nT, rb, gamma));
+        if (!have_nh) PPS_TRY(tr(ab + h->lay.g[b], f, hT, nullptr, nullptr, ab + h->lay.u[b]));
         PPS_TRY(tr(dy, d, dyT));
-        PPS_TRY(tr(sn, d, nT));
-        if (!have_nh) PPS_TRY(tr(dgu, 2 * f, dguT));
+        if (!have_nh && !entry_dguT) PPS_TRY(tr(dgu, 2 * f, dguT));
         a.seg[0].A = hT; a.seg[0].lda = Tp; a.seg[0].B = dyT; a.seg[0].ldb = Tp;
-        c.seg[0].A = nT; c.seg[0].lda = Tp; c.seg[0].B = dguT; c.seg[0].ldb = Tp;
+        c.seg[0].A = nT; c.seg[0].lda = Tp; c.seg[0].B = entry_dguT ? dgu : dguT; c.seg[0].ldb = Tp;
         a.a_kcontig = a.b_kcontig = c.a_kcontig = c.b_kcontig = true;
     }
     a.epi = pps::EPI_ACC_F32;
@@ -451,7 +458,9 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
         if (h->split) {
             dy = sb + h->lay.dy[b];
             dx = b == 0 ? dx_out : static_cast<void*>(sb + h->lay.dy[b - 1]);
-            dgu = sb + h->lay.dgu[b];
+            // full tiles: the entry keeps dg|du T-contiguous (written by the
+            // dh epilogue below) and dn reads the row-major copy in scratch
+            dgu = hT_fused(h) ? h->scratch + h->s_dgu : sb + h->lay.dgu[b];
         } else {
             dy = b == D.L - 1 ? dy_in : static_cast<const void*>(dxbuf[(b + 1) & 1]);
             dx = b == 0 ? dx_out : static_cast<void*>(dxbuf[b & 1]);
@@ -477,6 +486,9 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
             a.e.out2 = fused ? h->scratch + h->s_hT : nullptr;
             a.e.out3 = fused ? h->scratch + h->s_dguT : nullptr;
             a.e.ld2 = h->Tp;
+        } else if (h->tn && h->split && hT_fused(h)) {
+            a.e.out3 = sb + h->lay.dgu[b];
+            a.e.ld2 = h->Tp;
         }
         PPS_TRY(timed(h, PPS_K_DH, gemm_flops(T, f, d), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
         // dn = dg Wg^T + du Wu^T (one accumulator, K = 2 ffn).
@@ -489,13 +501,15 @@ int swiglu_backward(pps_stage* h, int slot, int chunk, const void* dy_in, void* 
         c.e.out0 = dn; c.e.ld0 = d;
         PPS_TRY(timed(h, PPS_K_DN, gemm_flops(T, d, 2.0 * f), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
         // RMSNorm backward + residual, dgamma partials, then their fixed-order
-        // sum; without the split, also n for this block's weight gradient.
+        // sum; fp32 without the split, also n for this block's weight gradient.
         int nrows = 0;
+        // n row-major only for the fp32 weight gradients (bf16 takes nT from x)
+        char* n_out = h->tn ? nullptr : sn;
         PPS_TRY(timed(h, PPS_K_RMSNORM_BWD, 0.0,
-                      (double)T * d * 4 + (sn ? 4.0 : 3.0) * T * d * es + T * 4.0 + d * 4.0 +
+                      (double)T * d * 4 + (n_out ? 4.0 : 3.0) * T * d * es + T * 4.0 + d * 4.0 +
                           (double)pps::rmsnorm_bwd_partial_rows(T) * d * 4, [&] {
                           return pps::rmsnorm_bwd(dt, dn, act_x(h, slot, b), reinterpret_cast<const float*>(ab + h->lay.r[b]),
-                                                  gamma, dy, T, d, dx, part, &nrows, sn, h->stream);
+                                                  gamma, dy, T, d, dx, part, &nrows, n_out, h->stream);
                       }));
         const int prow = pps::rmsnorm_bwd_partial_rows(T);
         PPS_TRY(timed(h, PPS_K_DGAMMA, 0.0, (double)prow * d * 4 + 8.0 * d, [&] {
@@ -655,7 +669,10 @@ int create_stage(const pps_stage_desc* desc, pps_stage** out, bool noalloc) {
     if (h->swiglu) {
         take(h->s_n, T * dm * h->es);
         take(h->s_h, T * f * h->es);
-        take(h->s_dgu, h->split ? 256 : T * 2 * f * h->es);
+        // the split keeps dg|du in the entry; on full tiles the entry holds
+        // it T-contiguous and dn reads a row-major copy from here
+        const bool fused_t = h->tn && desc->T % 256 == 0 && desc->ffn % 256 == 0;
+        take(h->s_dgu, h->split && !fused_t ? 256 : T * 2 * f * h->es);
         take(h->s_dn, T * dm * 4);
         take(h->s_part, (size_t)pps::rmsnorm_bwd_partial_rows((int64_t)T) * dm * 4);
         if (h->tn) {

@@ -80,9 +80,12 @@ def test_swiglu_stage_parity(env, dtype, kind):
     _check(cfg, got, inp, TOL[dtype])
 
 
-def test_split_is_bit_identical_to_unsplit(env):
+@pytest.mark.parametrize("shape", ["ragged", "full_tiles"])
+def test_split_is_bit_identical_to_unsplit(env, shape):
+    # full tiles: both runs take dg|du T-contiguous from the dh epilogue (the
+    # split keeps it in the entry until W), ragged: both copy it
     from pipeline_schedules_amd.inputs import make_inputs
-    cfg = _swiglu_cfg("bf16", M=5, P=3)
+    cfg = _swiglu_cfg("bf16", M=5, P=3) if shape == "ragged" else _swiglu_cfg("bf16", T=512, d=264, f=512, M=5, P=3)
     inp = make_inputs(cfg, gamma="random")
     a = _run_single(env, cfg, inp, "1f1b")
     b = _run_single(env, cfg, inp, "zb1p")
