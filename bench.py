@@ -36,10 +36,10 @@ PEAK_HBM_GBS = 8000.0
 # copy kernel measured in the same runs).  Valid only for the GEMM source they were taken on.
 TRAFFIC = {
     "config": "c3_80layer_p8_stage0",
-    "gemm_source_sha1": "828caa5a13b7543d069455a141e85f1090ecaabd",
+    "gemm_source_sha1": "308019521a558e81510d9d5f411368f887aaf54e",
     "bytes_per_launch": {
-        "gemm_gateup_swiglu": 13.775e9, "gemm_down_residual": 6.012e9, "gemm_dh_swiglu_bwd": 8.653e9,
-        "gemm_dn": 12.583e9, "gemm_wgrad_down": 8.654e9, "gemm_wgrad_gateup": 8.654e9,
+        "gemm_gateup_swiglu": 13.388e9, "gemm_down_residual": 6.079e9, "gemm_dh_swiglu_bwd": 9.418e9,
+        "gemm_dn": 12.749e9, "gemm_wgrad_down": 8.948e9, "gemm_wgrad_gateup": 8.948e9,
     },
 }
 
