@@ -3,8 +3,8 @@
 // Layout: C[m,n] = sum_k A(m,k) B(n,k) with both operands K-contiguous
 // ("TN"): A row-major [M, K] (stride lda), B [N, K] (ldb).  The forward reads
 // per-pass K-contiguous copies of the weights; the weight-gradient GEMMs
-// dW = X^T Y reduce over tokens and read T-contiguous copies of the
-// activations and gradients.  The kernel tiles 256 x 256 x 64, takes both
+// dW = X^T Y reduce over tokens and read T-contiguous activations and
+// gradients (copies, or written so by the SwiGLU-backward epilogue).  The kernel tiles 256 x 256 x 64, takes both
 // operands straight from memory into LDS (direct-to-LDS buffer loads, no
 // register staging) and reads zeros outside an operand's extent, which pads
 // ragged M, N and K tails.
