@@ -4,10 +4,10 @@
 // ("TN"): A row-major [M, K] (stride lda), B [N, K] (ldb).  The forward reads
 // per-pass K-contiguous copies of the weights; the weight-gradient GEMMs
 // dW = X^T Y reduce over tokens and read T-contiguous activations and
-// gradients (copies, or written so by the SwiGLU-backward epilogue).  The kernel tiles 256 x 256 x 64, takes both
-// operands straight from memory into LDS (direct-to-LDS buffer loads, no
-// register staging) and reads zeros outside an operand's extent, which pads
-// ragged M, N and K tails.
+// gradients (copies, or written so by the SwiGLU-backward epilogue).  The
+// kernel tiles 256 x 256 x 64, takes both operands straight from memory into
+// LDS (direct-to-LDS buffer loads, no register staging) and reads zeros
+// outside an operand's extent, which pads ragged M, N and K tails.
 //
 // Kernel: 256 threads = 4 wavefronts in a 2 x 2 grid, one per SIMD,
 // 128 x 128 per wavefront = 8 x 8 tiles of v_mfma_f32_16x16x32_bf16 (256
