@@ -39,6 +39,7 @@
 // ids are remapped so each XCD gets a contiguous run of logical tiles, and
 // logical tiles are ordered in groups of 8 tile-rows so the tiles running on
 // one XCD share A rows and B columns in that XCD's L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "epilogue.h"
@@ -599,9 +600,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     else run(std::false_type{});
 }
 
-// Byte extent of a row-major operand: (rows-1)*ld + cols elements of bf16.
+// Byte extent of a row-major operand: (rows-1)*ld + cols' elements of bf16,
+// cols' = cols rounded up to the 8-element chunk the loader moves (within
+// ld).  The buffer range check works on whole dwords, so an extent that ended
+// inside the last row's chunk (cols odd: a K = T of odd length) would drop
+// that row's last valid element; the elements of [cols, cols') are the
+// row's padding, which the K-tail chunks of every other row read as well
+// (zero in the T-contiguous operands).
 inline bool extent(int64_t rows, int64_t ld, int64_t cols, uint32_t& out) {
-    const int64_t b = rows <= 0 ? 0 : ((rows - 1) * ld + cols) * 2;
+    const int64_t cr = std::min<int64_t>((cols + 7) / 8 * 8, std::max<int64_t>(ld, cols));
+    const int64_t b = rows <= 0 ? 0 : ((rows - 1) * ld + cr) * 2;
     if (b >= (int64_t)OOB) return false;
     out = (uint32_t)b;
     return true;
