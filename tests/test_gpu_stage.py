@@ -262,6 +262,21 @@ def test_extreme_shapes(env, name, dtype, T, d, f, L):
     _check(cfg, got, inp, TOL[dtype])
 
 
+# Degenerate pipelines: a single stage (P = 1: F and B alternate, one stash
+# slot), a single micro-batch, and the last stage of a deeper pipeline
+# (k = P-1: warmup of one), under 1F1B and the Zero-Bubble split.
+@pytest.mark.parametrize("P,M,k,kind", [(1, 3, 0, "1f1b"), (2, 1, 0, "1f1b"), (4, 5, 3, "1f1b"),
+                                        (4, 5, 3, "zb1p"), (1, 2, 0, "zb2p")])
+def test_degenerate_pipelines(env, P, M, k, kind):
+    from pipeline_schedules_amd.inputs import make_inputs
+    cfg = _swiglu_cfg("bf16", T=136, d=264, f=392, L=2, M=M, P=P, k=k)
+    inp = make_inputs(cfg, gamma="random")
+    got = _run_single(env, cfg, inp, kind)
+    _check(cfg, got, inp, TOL["bf16"])
+    ops = S.stage_ops(P, M, k, 1, _oracle_kind(kind))
+    assert got[3]["peak_live_entries"] == max(o[4] for o in ops)
+
+
 def test_empty_microbatch(env):
     torch, pps, G = env
     from pipeline_schedules_amd.inputs import make_inputs
