@@ -255,8 +255,10 @@ int pps_stage_zero_grad(pps_stage* h);
 
 /* Gradient buffer of (chunk, block): which = 0 dWg [d,ffn], 1 dWu [d,ffn],
    2 dWd [ffn,d], 3 dgamma [d] (SwiGLU); 0 dW [d,d], 1 db [d] (toy).  fp32,
-   library-owned, valid until destroy.  PPS_EINVAL out of range or with
-   PPS_FLAG_BOOKKEEPING_ONLY. */
+   library-owned, valid until destroy.  Its contents are written by work on
+   the handle's stream: read them on that stream, or after pps_stage_sync
+   with the read ordered on the reader's own stream.  PPS_EINVAL out of range
+   or with PPS_FLAG_BOOKKEEPING_ONLY. */
 int pps_stage_get_grad(const pps_stage* h, int chunk, int block, int which, const float** dptr);
 
 /* Wait for the handle's stream; surfaces asynchronous HIP errors as PPS_EHIP. */

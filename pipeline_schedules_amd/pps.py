@@ -234,13 +234,19 @@ class Stage:
         return p.value
 
     def grad(self, chunk, block, which, shape):
-        """Copy a gradient buffer into a new fp32 torch tensor on the current device."""
+        """Copy a gradient buffer into a new fp32 torch tensor on the current device.  The copy
+        runs on the caller's current stream once the stage's stream has finished, so later work on
+        that stream sees it (a synchronous device-to-device hipMemcpy is not ordered with a
+        non-default stream)."""
         import torch
         out = torch.empty(shape, dtype=torch.float32, device="cuda")
         self.sync()
         src = self.grad_ptr(chunk, block, which)
-        _hip().hipMemcpy(ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(src),
-                         ctypes.c_size_t(out.numel() * 4), 3)
+        rc = _hip().hipMemcpyAsync(ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(src),
+                                   ctypes.c_size_t(out.numel() * 4), 3,
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpyAsync of a gradient failed (hipError {rc})")
         return out
 
     def stats(self):
@@ -275,8 +281,9 @@ def _hip():
     if _hiplib is None:
         _hiplib = ctypes.CDLL("libamdhip64.so.7", mode=ctypes.RTLD_GLOBAL | os.RTLD_NOLOAD) \
             if hasattr(os, "RTLD_NOLOAD") else ctypes.CDLL("libamdhip64.so.7")
-        _hiplib.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
-        _hiplib.hipMemcpy.restype = ctypes.c_int
+        _hiplib.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                           ctypes.c_void_p]
+        _hiplib.hipMemcpyAsync.restype = ctypes.c_int
     return _hiplib
 
 

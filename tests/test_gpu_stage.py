@@ -277,6 +277,26 @@ def test_degenerate_pipelines(env, P, M, k, kind):
     assert got[3]["peak_live_entries"] == max(o[4] for o in ops)
 
 
+def test_side_stream_bit_identical(env):
+    # Every launch goes to the stream the stage was created with: the same
+    # pass on a separate (non-default, default-priority) stream gives the same
+    # bits as on the current one.
+    torch, pps, G = env
+    from pipeline_schedules_amd.inputs import make_inputs
+    cfg = _swiglu_cfg("bf16", T=264, d=264, f=392, L=2, M=4, P=2)
+    inp = make_inputs(cfg, gamma="random")
+    a = _run_single(env, cfg, inp, "zb1p")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        b = _run_single(env, cfg, inp, "zb1p")
+    torch.cuda.synchronize()
+    for i in range(cfg.M):
+        assert np.array_equal(a[0][i], b[0][i]) and np.array_equal(a[1][i], b[1][i])
+    for blk in range(cfg.L):
+        for key in a[2][blk]:
+            assert np.array_equal(a[2][blk][key], b[2][blk][key]), key
+
+
 def test_empty_microbatch(env):
     torch, pps, G = env
     from pipeline_schedules_amd.inputs import make_inputs
