@@ -191,33 +191,33 @@ def test_toy_stage_parity(env, kind):
     _check(C1_TOY, got, inp, TOL["fp32"])
 
 
-@pytest.mark.parametrize("shape", ["ragged", "full_tiles"])
+@pytest.mark.parametrize("shape,v,k", [("ragged", 2, 0), ("full_tiles", 2, 0), ("ragged", 3, 0), ("ragged", 3, 1),
+                                       ("ragged", 4, 1)])
 @pytest.mark.parametrize("recompute", [False, True])
-def test_interleaved_stage_parity(env, recompute, shape):
+def test_interleaved_stage_parity(env, recompute, shape, v, k):
     # "full_tiles": T and ffn multiples of the 256 x 256 GEMM tile, so the dh
     # epilogue writes h transposed for dW_d under chunked stashing.
     torch, pps, G = env
     from pipeline_schedules_amd.inputs import make_inputs
     if shape == "ragged":
-        cfg = _swiglu_cfg("bf16", T=264, d=264, f=392, L=1, M=4, P=2, k=0, v=2)
+        cfg = _swiglu_cfg("bf16", T=264, d=264, f=392, L=1, M=4, P=2, k=k, v=v)
     else:
-        cfg = _swiglu_cfg("bf16", T=512, d=264, f=512, L=2, M=4, P=2, k=0, v=2)
+        cfg = _swiglu_cfg("bf16", T=512, d=264, f=512, L=2, M=4, P=2, k=k, v=v)
     inp = make_inputs(cfg, gamma="random")
-    rng = np.random.default_rng(5)
-    # independent seeded inputs for chunk 1 (its real input comes from another device)
-    xs1 = [np.asarray(x) for x in make_inputs(cfg, rng_seed=1).xs]
-    gs1 = [np.asarray(g) for g in make_inputs(cfg, rng_seed=2).Gs]
+    # independent seeded inputs for chunks c > 0 (their real input comes from another device)
+    cin = [(inp.xs, inp.Gs)] + [([np.asarray(x) for x in make_inputs(cfg, rng_seed=2 * c - 1).xs],
+                                 [np.asarray(g) for g in make_inputs(cfg, rng_seed=2 * c).Gs]) for c in range(1, v)]
     w = G.upload_params(inp.params[0], "swiglu", "bf16")
     st = pps.stage_from_config(cfg, weights=w, stream=torch.cuda.current_stream(),
                                flags=pps.FLAG_RECOMPUTE if recompute else 0)
-    ops = pps.make_schedule(cfg.P, cfg.M, cfg.k, 2, pps.ONE_F_ONE_B)
-    assert ops == [tuple(o) for o in S.stage_ops(cfg.P, cfg.M, cfg.k, 2, S.ONE_F_ONE_B)]
-    xs = [[G.to_dev(x, "bf16") for x in inp.xs], [G.to_dev(x, "bf16") for x in xs1]]
-    dys = [[G.to_dev(g, "bf16") for g in inp.Gs], [G.to_dev(g, "bf16") for g in gs1]]
+    ops = pps.make_schedule(cfg.P, cfg.M, cfg.k, v, pps.ONE_F_ONE_B)
+    assert ops == [tuple(o) for o in S.stage_ops(cfg.P, cfg.M, cfg.k, v, S.ONE_F_ONE_B)]
+    xs = [[G.to_dev(x, "bf16") for x in cx] for cx, _ in cin]
+    dys = [[G.to_dev(g, "bf16") for g in cg] for _, cg in cin]
     ys, dxs = G.run_stage(st, ops, xs, dys, cfg.T, cfg.d, "bf16")
     assert st.oplog() == ops
     assert st.stats()["peak_live_entries"] == max(o[4] for o in ops)
-    for c, (cx, cg) in enumerate([(inp.xs, inp.Gs), (xs1, gs1)]):
+    for c, (cx, cg) in enumerate(cin):
         ry, rdx, rg = N.full_batch_step(cx, cg, inp.params[0][c * cfg.L:(c + 1) * cfg.L], "swiglu", cfg.eps)
         for i in range(cfg.M):
             assert N.rel_l2(G.to_host(ys[c][i]), ry[i]) <= TOL["bf16"]
@@ -295,6 +295,40 @@ def test_side_stream_bit_identical(env):
     for blk in range(cfg.L):
         for key in a[2][blk]:
             assert np.array_equal(a[2][blk][key], b[2][blk][key]), key
+
+
+def test_weights_changed_between_passes_take_effect(env):
+    # The library's K-contiguous weight copies are refreshed at the first F of
+    # each pass, so weights the caller changes between passes are used.
+    torch, pps, G = env
+    from pipeline_schedules_amd.inputs import make_inputs
+    cfg = _swiglu_cfg("bf16", T=264, d=264, f=392, L=2, M=2, P=2)
+    inp = make_inputs(cfg, gamma="random")
+    w = G.upload_params(inp.params[0], "swiglu", "bf16")
+    st = pps.stage_from_config(cfg, weights=w, stream=torch.cuda.current_stream())
+    ops = pps.make_schedule(cfg.P, cfg.M, cfg.k)
+    xs = [[G.to_dev(x, "bf16") for x in inp.xs]]
+    dys = [[G.to_dev(g, "bf16") for g in inp.Gs]]
+    G.run_stage(st, ops, xs, dys, cfg.T, cfg.d, "bf16")
+    # in place, exactly representable: matrices x 0.5 (bf16), gamma x 1.5 (fp32)
+    params2 = []
+    for b, p in enumerate(inp.params[0]):
+        for j, key in enumerate(("Wg", "Wu", "Wd")):
+            w[4 * b + j].mul_(0.5)
+        w[4 * b + 3].mul_(1.5)
+        params2.append({"Wg": p["Wg"] * 0.5, "Wu": p["Wu"] * 0.5, "Wd": p["Wd"] * 0.5,
+                        "gamma": (p["gamma"].astype(np.float32) * np.float32(1.5))})
+    st.zero_grad()
+    ys, dxs = G.run_stage(st, ops, xs, dys, cfg.T, cfg.d, "bf16")
+    ry, rdx, rg = N.full_batch_step(inp.xs, inp.Gs, params2, "swiglu", cfg.eps)
+    for i in range(cfg.M):
+        assert N.rel_l2(G.to_host(ys[0][i]), ry[i]) <= TOL["bf16"]
+        assert N.rel_l2(G.to_host(dxs[0][i]), rdx[i]) <= TOL["bf16"]
+    got = G.stage_grads(st, cfg.L, "swiglu", cfg.d, cfg.f)
+    for b in range(cfg.L):
+        for key in rg[b]:
+            assert N.rel_l2(got[b][key], rg[b][key]) <= TOL["bf16"], (b, key)
+    st.close()
 
 
 def test_empty_microbatch(env):
