@@ -240,6 +240,7 @@ def main():
     dx = torch.empty((T, d), dtype=tdt, device=dev)
 
     def one_pass():
+        st.zero_grad()   # a pass starts from zero gradients, as a training step would
         for op, mb, c, *_ in ops:
             if op == pps.OP_F:
                 st.forward(mb, c, chunk_x[c][mb], y)
@@ -248,7 +249,6 @@ def main():
             else:
                 st.backward_weight(mb, c)
 
-    st.zero_grad()
     _log(f"warmup: {args.warmup} pass(es) of {len(ops)} ops")
     for _ in range(args.warmup):
         one_pass()
