@@ -29,7 +29,7 @@ def _emulate(cfg, kind="1f1b", gamma=None, bias=None):
         s = st.stats()
         sched = pps.make_schedule(cfg.P, cfg.M, k, 1, pps.KIND_BY_NAME[kind])
         assert s["peak_live_entries"] == max(o[4] for o in sched)
-        if kind != "zb1p":
+        if kind not in ("zb1p", "zb2p"):
             assert s["peak_live_entries"] == (cfg.M if kind == "gpipe" else min(cfg.P - k, cfg.M))
         st.close()
     rys, rdxs, rgrads = N.pipeline_model_step(inp.xs, inp.Gs, inp.params, cfg.block, cfg.eps)
@@ -44,7 +44,7 @@ def _emulate(cfg, kind="1f1b", gamma=None, bias=None):
     return errs
 
 
-@pytest.mark.parametrize("kind", ["1f1b", "gpipe", "zb1p"])
+@pytest.mark.parametrize("kind", ["1f1b", "gpipe", "zb1p", "zb2p"])
 def test_emulation_toy_two_stages(kind):
     # 2 stages x 4 micro-batches, each stage 2 x (Linear 64->64 + GELU), fp32.
     from pipeline_schedules_amd.configs import C1_TOY
@@ -63,9 +63,11 @@ def test_emulation_swiglu_four_stages():
     assert not bad, bad
 
 
-def test_emulation_swiglu_zb1p_small():
+@pytest.mark.parametrize("kind,T", [("zb1p", 264), ("zb2p", 264), ("zb2p", 256)])
+def test_emulation_swiglu_zb_small(kind, T):
+    # T = 256: full tiles, so every stage keeps dg|du T-contiguous in its entries
     from pipeline_schedules_amd.configs import C2_SMALL
-    cfg = C2_SMALL.with_(P=4, M=8, d=256, f=512, T=264, L=1, kind="zb1p")
-    errs = _emulate(cfg, "zb1p", gamma="random")
+    cfg = C2_SMALL.with_(P=4, M=8, d=256, f=512, T=T, L=1, kind=kind)
+    errs = _emulate(cfg, kind, gamma="random")
     bad = {k: v for k, v in errs.items() if not v <= 2e-2}
     assert not bad, bad
