@@ -250,15 +250,17 @@ def test_zero_down_projection_closed_form(env):
 # smallest widths the ABI accepts (d = ffn = 8: every K is a partial tile), and
 # the largest model width (d = 16384: the widest RMSNorm kernels, full tiles
 # with the fused T-contiguous outputs).
-@pytest.mark.parametrize("name,dtype,T,d,f,L", [
-    ("one_token", "bf16", 1, 264, 392, 2), ("one_token", "fp32", 1, 264, 392, 2),
-    ("minimum_width", "bf16", 37, 8, 8, 2), ("minimum_width", "fp32", 37, 8, 8, 2),
-    ("maximum_width", "bf16", 256, 16384, 512, 1)])
-def test_extreme_shapes(env, name, dtype, T, d, f, L):
+@pytest.mark.parametrize("name,dtype,T,d,f,L,kind,flags", [
+    ("one_token", "bf16", 1, 264, 392, 2, "1f1b", 0), ("one_token", "fp32", 1, 264, 392, 2, "1f1b", 0),
+    ("one_token", "bf16", 1, 264, 392, 2, "zb1p", 0), ("odd_tokens", "bf16", 77, 264, 392, 2, "1f1b", "recompute"),
+    ("minimum_width", "bf16", 37, 8, 8, 2, "1f1b", 0), ("minimum_width", "fp32", 37, 8, 8, 2, "1f1b", 0),
+    ("maximum_width", "bf16", 256, 16384, 512, 1, "1f1b", 0)])
+def test_extreme_shapes(env, name, dtype, T, d, f, L, kind, flags):
+    _, pps, _ = env
     from pipeline_schedules_amd.inputs import make_inputs
     cfg = _swiglu_cfg(dtype, T=T, d=d, f=f, L=L, M=3, P=2)
     inp = make_inputs(cfg, gamma="random")
-    got = _run_single(env, cfg, inp, "1f1b")
+    got = _run_single(env, cfg, inp, kind, flags=pps.FLAG_RECOMPUTE if flags == "recompute" else 0)
     _check(cfg, got, inp, TOL[dtype])
 
 
