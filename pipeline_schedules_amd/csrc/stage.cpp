@@ -671,8 +671,7 @@ int create_stage(const pps_stage_desc* desc, pps_stage** out, bool noalloc) {
         take(h->s_h, T * f * h->es);
         // the split keeps dg|du in the entry; on full tiles the entry holds
         // it T-contiguous and dn reads a row-major copy from here
-        const bool fused_t = h->tn && desc->T % 256 == 0 && desc->ffn % 256 == 0;
-        take(h->s_dgu, h->split && !fused_t ? 256 : T * 2 * f * h->es);
+        take(h->s_dgu, h->split && !hT_fused(h) ? 256 : T * 2 * f * h->es);
         take(h->s_dn, T * dm * 4);
         take(h->s_part, (size_t)pps::rmsnorm_bwd_partial_rows((int64_t)T) * dm * 4);
         if (h->tn) {
