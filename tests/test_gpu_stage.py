@@ -333,6 +333,53 @@ def test_weights_changed_between_passes_take_effect(env):
     st.close()
 
 
+def test_two_stages_on_two_streams(env):
+    # Two handles, each on its own stream, their ops issued interleaved: each
+    # gives the bits it gives alone (no state shared between handles).
+    torch, pps, G = env
+    from pipeline_schedules_amd.inputs import make_inputs
+    cfgs = [_swiglu_cfg("bf16", T=264, d=264, f=392, L=2, M=4, P=2),
+            _swiglu_cfg("bf16", T=256, d=256, f=512, L=1, M=3, P=3, k=1)]
+    kinds = ["1f1b", "zb1p"]
+    inps = [make_inputs(c, gamma="random") for c in cfgs]
+    alone = [_run_single(env, c, i, k) for c, i, k in zip(cfgs, inps, kinds)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    runs = []
+    for cfg, inp, kind, s in zip(cfgs, inps, kinds, streams):
+        with torch.cuda.stream(s):
+            w = G.upload_params(inp.params[0], "swiglu", "bf16")
+            st = pps.stage_from_config(cfg, weights=w, kind=kind, stream=s)
+            xs = [G.to_dev(x, "bf16") for x in inp.xs]
+            dys = [G.to_dev(g, "bf16") for g in inp.Gs]
+            ys = [torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda") for _ in range(cfg.M)]
+            dxs = [torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda") for _ in range(cfg.M)]
+        ops = pps.make_schedule(cfg.P, cfg.M, cfg.k, 1, pps.KIND_BY_NAME[kind])
+        runs.append({"st": st, "w": w, "xs": xs, "dys": dys, "ys": ys, "dxs": dxs, "ops": list(ops), "s": s})
+    while any(r["ops"] for r in runs):
+        for r in runs:
+            if r["ops"]:
+                op, mb, c, *_ = r["ops"].pop(0)
+                if op == pps.OP_F:
+                    r["st"].forward(mb, c, r["xs"][mb], r["ys"][mb])
+                elif op == pps.OP_B:
+                    r["st"].backward(mb, c, r["dys"][mb], r["dxs"][mb])
+                else:
+                    r["st"].backward_weight(mb, c)
+    for r, cfg, ref in zip(runs, cfgs, alone):
+        with torch.cuda.stream(r["s"]):
+            r["st"].sync()
+            grads = G.stage_grads(r["st"], cfg.L, "swiglu", cfg.d, cfg.f)
+            ys = [G.to_host(y) for y in r["ys"]]
+            dxs = [G.to_host(x) for x in r["dxs"]]
+        for i in range(cfg.M):
+            assert np.array_equal(ys[i], ref[0][i]) and np.array_equal(dxs[i], ref[1][i])
+        for blk in range(cfg.L):
+            for key in ref[2][blk]:
+                assert np.array_equal(grads[blk][key], ref[2][blk][key]), key
+        r["st"].close()
+    torch.cuda.synchronize()
+
+
 def test_empty_microbatch(env):
     torch, pps, G = env
     from pipeline_schedules_amd.inputs import make_inputs
