@@ -27,6 +27,11 @@
  *     row-major [in, out], so a layer computes Y = X W.
  *   - Work is enqueued asynchronously on the handle's stream; a handle is
  *     single-threaded and must not be used from two host threads at once.
+ *   - pps_stage_zero_grad, pps_stage_forward, pps_stage_backward and
+ *     pps_stage_backward_weight (profiling off) only launch kernels on the
+ *     handle's stream: no allocation, memset, copy call or synchronisation,
+ *     so a pass may be recorded into a HIP graph on that stream and replayed.
+ *     The handle's host-side bookkeeping advances once, during recording.
  *   - Constraints: d % 8 == 0 and ffn % 8 == 0 (16-byte rows); d <= 16384;
  *     T >= 0 (T == 0 is accepted and computes nothing).
  */

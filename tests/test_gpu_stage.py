@@ -380,6 +380,58 @@ def test_two_stages_on_two_streams(env):
     torch.cuda.synchronize()
 
 
+def test_pass_captured_in_a_hip_graph(env):
+    # A whole pass (gradient zeroing and the op list) recorded into a HIP graph
+    # and replayed: the library launches only kernels on the stage's stream
+    # during ops (zeroing by a fill kernel, no allocation, no memset), so every
+    # replay reproduces the eager pass bit for bit.  Eager work and
+    # synchronisation run between the replays.
+    torch, pps, G = env
+    from pipeline_schedules_amd.inputs import make_inputs
+    cfg = _swiglu_cfg("bf16", T=264, d=264, f=392, L=2, M=4, P=2)
+    inp = make_inputs(cfg, gamma="random")
+    ref = _run_single(env, cfg, inp, "zb1p")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        w = G.upload_params(inp.params[0], "swiglu", "bf16")
+        st = pps.stage_from_config(cfg, weights=w, kind="zb1p", stream=s)
+        xs = [G.to_dev(x, "bf16") for x in inp.xs]
+        dys = [G.to_dev(g, "bf16") for g in inp.Gs]
+        ys = [torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda") for _ in range(cfg.M)]
+        dxs = [torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda") for _ in range(cfg.M)]
+    s.synchronize()
+    ops = pps.make_schedule(cfg.P, cfg.M, cfg.k, 1, pps.ZB1P)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        st.zero_grad()
+        for op, mb, c, *_ in ops:
+            if op == pps.OP_F:
+                st.forward(mb, c, xs[mb], ys[mb])
+            elif op == pps.OP_B:
+                st.backward(mb, c, dys[mb], dxs[mb])
+            else:
+                st.backward_weight(mb, c)
+    for rep in range(3):
+        for t in ys + dxs:   # clobber the outputs between replays
+            t.fill_(rep + 1.0)
+        junk = torch.randn((1024, 1024), device="cuda") @ torch.randn((1024, 1024), device="cuda")
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            grads = G.stage_grads(st, cfg.L, "swiglu", cfg.d, cfg.f)
+            got_y = [G.to_host(y) for y in ys]
+            got_dx = [G.to_host(x) for x in dxs]
+        s.synchronize()
+        for i in range(cfg.M):
+            assert np.array_equal(got_y[i], ref[0][i]) and np.array_equal(got_dx[i], ref[1][i]), (rep, i)
+        for blk in range(cfg.L):
+            for key in ref[2][blk]:
+                assert np.array_equal(grads[blk][key], ref[2][blk][key]), (rep, blk, key)
+        del junk
+    st.close()
+
+
 def test_empty_microbatch(env):
     torch, pps, G = env
     from pipeline_schedules_amd.inputs import make_inputs
