@@ -240,8 +240,9 @@ int pps_stage_forward(pps_stage* h, int mb, int chunk, const void* x_in, void* y
  * accumulate dW into the fp32 gradient buffers and free the slot; ZB
  * schedules compute only dX (and dgamma) and keep the slot for W
  * ([GPipe->ZB Zero Bubble]: B = G W^T now, W = X^T G later).
- * Errors: PPS_ENOENT if mb has no saved forward; PPS_ESTATE if mb was
- * already backwarded; PPS_EORDER if it is not the schedule's next backward
+ * Errors: PPS_ENOENT if mb has no saved forward in the current pass (also
+ * right after a completed pass); PPS_ESTATE if mb was already backwarded in
+ * this pass; PPS_EORDER if it is not the schedule's next backward
  * (for 1F1B: the oldest saved entry); PPS_EINVAL on NULL pointers.
  */
 int pps_stage_backward(pps_stage* h, int mb, int chunk, const void* dy_in, void* dx_out);

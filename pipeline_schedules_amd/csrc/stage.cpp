@@ -825,7 +825,9 @@ extern "C" int pps_stage_backward(pps_stage* h, int mb, int chunk, const void* d
     if (mb < 0 || mb >= h->d.M || chunk < 0 || chunk >= h->d.v) return PPS_EINVAL;
     if (!h->bookkeeping && (!dy_in || !dx_out)) return PPS_EINVAL;
     const size_t key = (size_t)chunk * h->d.M + mb;
-    if (h->status[key] == ST_NONE) return PPS_ENOENT;
+    // after a completed pass nothing of the next one is saved yet
+    const bool pass_done = h->fpos == h->fseq.size() && h->bpos == h->bseq.size() && h->wpos == h->wseq.size();
+    if (pass_done || h->status[key] == ST_NONE) return PPS_ENOENT;
     if (h->status[key] != ST_F) return PPS_ESTATE;
     if (h->bpos >= h->bseq.size() || h->bseq[h->bpos] != std::make_pair(mb, chunk)) return PPS_EORDER;
     const int slot = h->slot_of[key];

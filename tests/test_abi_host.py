@@ -235,6 +235,14 @@ def test_bookkeeping_error_codes():
     zb.close()
     zb2.close()
 
+    # after a completed pass, a backward before the next pass's forward has nothing saved
+    st = _bk_stage(P, M, 0)
+    _drive(st, S.stage_ops(P, M, 0))
+    assert st.backward_status(0, 0, None, None) == pps.ENOENT
+    st.forward(0, 0, None, None)                            # starts the next pass
+    assert st.oplog() == [tuple(o) for o in S.stage_ops(P, M, 0)[:1]]
+    st.close()
+
 
 def test_create_rejects_bad_descs():
     _lib_or_skip()
