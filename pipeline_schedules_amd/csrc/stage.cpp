@@ -785,11 +785,15 @@ extern "C" int pps_stage_create_noalloc(const pps_stage_desc* desc, pps_stage** 
     return create_stage(desc, out, true);
 }
 
+// Caller buffers must be 16-byte aligned (the kernels move 16-byte pieces):
+// checked before anything is enqueued.
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 extern "C" int pps_stage_forward(pps_stage* h, int mb, int chunk, const void* x_in, void* y_out) {
     if (!h) return PPS_EINVAL;
     if (h->failed) return PPS_EHIP;
     if (mb < 0 || mb >= h->d.M || chunk < 0 || chunk >= h->d.v) return PPS_EINVAL;
-    if (!h->bookkeeping && (!x_in || !y_out)) return PPS_EINVAL;
+    if (!h->bookkeeping && (!x_in || !y_out || !aligned16(x_in) || !aligned16(y_out))) return PPS_EINVAL;
     // A call after a completed pass starts the next one.
     const bool next_pass = h->fpos == h->fseq.size() && h->bpos == h->bseq.size() && h->wpos == h->wseq.size();
     const size_t fpos = next_pass ? 0 : h->fpos;
@@ -823,7 +827,7 @@ extern "C" int pps_stage_backward(pps_stage* h, int mb, int chunk, const void* d
     if (!h) return PPS_EINVAL;
     if (h->failed) return PPS_EHIP;
     if (mb < 0 || mb >= h->d.M || chunk < 0 || chunk >= h->d.v) return PPS_EINVAL;
-    if (!h->bookkeeping && (!dy_in || !dx_out)) return PPS_EINVAL;
+    if (!h->bookkeeping && (!dy_in || !dx_out || !aligned16(dy_in) || !aligned16(dx_out))) return PPS_EINVAL;
     const size_t key = (size_t)chunk * h->d.M + mb;
     // after a completed pass nothing of the next one is saved yet
     const bool pass_done = h->fpos == h->fseq.size() && h->bpos == h->bseq.size() && h->wpos == h->wseq.size();

@@ -432,6 +432,47 @@ def test_pass_captured_in_a_hip_graph(env):
     st.close()
 
 
+def test_misaligned_buffers_rejected_before_any_work(env):
+    # Caller buffers must be 16-byte aligned: a misaligned one is rejected with
+    # EINVAL before anything is enqueued, the handle stays usable, and the
+    # pass then gives the same bits as a run that never saw the bad calls.
+    torch, pps, G = env
+    from pipeline_schedules_amd.inputs import make_inputs
+    cfg = _swiglu_cfg("bf16", T=264, d=264, f=392, L=2, M=2, P=2)
+    inp = make_inputs(cfg, gamma="random")
+    ref = _run_single(env, cfg, inp, "1f1b")
+    w = G.upload_params(inp.params[0], "swiglu", "bf16")
+    st = pps.stage_from_config(cfg, weights=w, stream=torch.cuda.current_stream())
+    xs = [G.to_dev(x, "bf16") for x in inp.xs]
+    dys = [G.to_dev(g, "bf16") for g in inp.Gs]
+    ys = [torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda") for _ in range(cfg.M)]
+    dxs = [torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda") for _ in range(cfg.M)]
+    spare = torch.empty(cfg.T * cfg.d + 8, dtype=torch.bfloat16, device="cuda")
+    bad = spare.data_ptr() + 2
+    assert st.forward_status(0, 0, bad, ys[0]) == pps.EINVAL
+    assert st.forward_status(0, 0, xs[0], bad) == pps.EINVAL
+    assert st.oplog() == []
+    ops = pps.make_schedule(cfg.P, cfg.M, cfg.k)
+    for i, (op, mb, c, *_) in enumerate(ops):
+        if op == pps.OP_F:
+            st.forward(mb, c, xs[mb], ys[mb])
+        else:
+            if i == 2:   # first backward: try the misaligned buffers first
+                assert st.backward_status(mb, c, bad, dxs[mb]) == pps.EINVAL
+                assert st.backward_status(mb, c, dys[mb], bad) == pps.EINVAL
+                assert len(st.oplog()) == i
+            st.backward(mb, c, dys[mb], dxs[mb])
+    st.sync()
+    assert st.oplog() == ops
+    grads = G.stage_grads(st, cfg.L, "swiglu", cfg.d, cfg.f)
+    for i in range(cfg.M):
+        assert np.array_equal(G.to_host(ys[i]), ref[0][i]) and np.array_equal(G.to_host(dxs[i]), ref[1][i])
+    for blk in range(cfg.L):
+        for key in ref[2][blk]:
+            assert np.array_equal(grads[blk][key], ref[2][blk][key]), key
+    st.close()
+
+
 def test_empty_microbatch(env):
     torch, pps, G = env
     from pipeline_schedules_amd.inputs import make_inputs
