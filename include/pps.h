@@ -226,7 +226,8 @@ int pps_stage_create_noalloc(const pps_stage_desc* desc, pps_stage** out);
  * blocks ([1F1B §5.2]: forward, then save the activations in the stash).
  * x_in [T,d] and y_out [T,d] are caller device buffers in the stage dtype.
  * What the backward needs is copied into a stash slot, so x_in may be
- * reused once the stream has passed this op.
+ * reused once the stream has passed this op; y_out may be x_in itself (every
+ * read of x_in precedes the last block's write of y_out on the stream).
  * Errors: PPS_EORDER if (mb, chunk) is not the schedule's next forward;
  * PPS_EFULL if no stash slot is free; PPS_EINVAL on NULL pointers or
  * pointers not 16-byte aligned (nothing is enqueued).
@@ -244,8 +245,9 @@ int pps_stage_forward(pps_stage* h, int mb, int chunk, const void* x_in, void* y
  * Errors: PPS_ENOENT if mb has no saved forward in the current pass (also
  * right after a completed pass); PPS_ESTATE if mb was already backwarded in
  * this pass; PPS_EORDER if it is not the schedule's next backward
- * (for 1F1B: the oldest saved entry); PPS_EINVAL on NULL pointers or
- * pointers not 16-byte aligned (nothing is enqueued).
+ * (for 1F1B: the oldest saved entry); PPS_EINVAL on NULL pointers,
+ * pointers not 16-byte aligned, or dy_in and dx_out overlapping (nothing is
+ * enqueued).
  */
 int pps_stage_backward(pps_stage* h, int mb, int chunk, const void* dy_in, void* dx_out);
 

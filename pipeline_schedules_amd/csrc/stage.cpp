@@ -828,6 +828,13 @@ extern "C" int pps_stage_backward(pps_stage* h, int mb, int chunk, const void* d
     if (h->failed) return PPS_EHIP;
     if (mb < 0 || mb >= h->d.M || chunk < 0 || chunk >= h->d.v) return PPS_EINVAL;
     if (!h->bookkeeping && (!dy_in || !dx_out || !aligned16(dy_in) || !aligned16(dx_out))) return PPS_EINVAL;
+    // dy_in is read again after dx_out is written (the weight gradients of the
+    // first block read it), so the two [T, d] buffers must not overlap
+    if (!h->bookkeeping && h->d.T > 0) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(dy_in), b = reinterpret_cast<uintptr_t>(dx_out);
+        const uintptr_t n = (uintptr_t)h->d.T * (uintptr_t)h->d.d * (uintptr_t)h->es;
+        if (a < b + n && b < a + n) return PPS_EINVAL;
+    }
     const size_t key = (size_t)chunk * h->d.M + mb;
     // after a completed pass nothing of the next one is saved yet
     const bool pass_done = h->fpos == h->fseq.size() && h->bpos == h->bseq.size() && h->wpos == h->wseq.size();

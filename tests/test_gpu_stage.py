@@ -473,6 +473,41 @@ def test_misaligned_buffers_rejected_before_any_work(env):
     st.close()
 
 
+@pytest.mark.parametrize("L", [1, 2])
+def test_forward_in_place_and_backward_overlap(env, L):
+    # y_out may be x_in itself (same bits as separate buffers); dy_in and dx_out
+    # must not overlap (the first block's weight gradient reads dy_in after
+    # dx_out is written): EINVAL, nothing enqueued.
+    torch, pps, G = env
+    from pipeline_schedules_amd.inputs import make_inputs
+    cfg = _swiglu_cfg("bf16", T=264, d=264, f=392, L=L, M=2, P=2)
+    inp = make_inputs(cfg, gamma="random")
+    ref = _run_single(env, cfg, inp, "1f1b")
+    w = G.upload_params(inp.params[0], "swiglu", "bf16")
+    st = pps.stage_from_config(cfg, weights=w, stream=torch.cuda.current_stream())
+    xs = [G.to_dev(x, "bf16") for x in inp.xs]       # overwritten by y in place
+    dys = [G.to_dev(g, "bf16") for g in inp.Gs]
+    dxs = [torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda") for _ in range(cfg.M)]
+    for op, mb, c, *_ in pps.make_schedule(cfg.P, cfg.M, cfg.k):
+        if op == pps.OP_F:
+            st.forward(mb, c, xs[mb], xs[mb])
+        else:
+            n = len(st.oplog())
+            assert st.backward_status(mb, c, dys[mb], dys[mb]) == pps.EINVAL
+            half = dys[mb].view(-1)[cfg.T * cfg.d // 2:]   # overlapping, 16-byte aligned
+            assert st.backward_status(mb, c, dys[mb], half) == pps.EINVAL
+            assert len(st.oplog()) == n
+            st.backward(mb, c, dys[mb], dxs[mb])
+    st.sync()
+    grads = G.stage_grads(st, cfg.L, "swiglu", cfg.d, cfg.f)
+    for i in range(cfg.M):
+        assert np.array_equal(G.to_host(xs[i]), ref[0][i]) and np.array_equal(G.to_host(dxs[i]), ref[1][i])
+    for blk in range(cfg.L):
+        for key in ref[2][blk]:
+            assert np.array_equal(grads[blk][key], ref[2][blk][key]), key
+    st.close()
+
+
 def test_empty_microbatch(env):
     torch, pps, G = env
     from pipeline_schedules_amd.inputs import make_inputs
