@@ -171,7 +171,10 @@ typedef struct pps_stage_desc {
     int32_t profile_capacity;   /* max kernel launches timed (PROFILE only)  */
     int32_t reserved;
     void*   stream;             /* hipStream_t; NULL = the null stream        */
-    /* Caller-owned device weights, read-only, must outlive the handle.
+    /* Caller-owned device weights, read-only, must outlive the handle and
+       stay unchanged during a pass (first forward to last backward or W:
+       bf16 forwards use library copies made at the pass's first forward,
+       backwards read these buffers); changes between passes are used.
        Index [(chunk*L + block)*nw + w]:
          SwiGLU (nw=4): Wg [d,ffn], Wu [d,ffn], Wd [ffn,d] in the stage dtype;
                         gamma [d] fp32.
