@@ -447,10 +447,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     // Whole tile inside M x N: every operand is a uniform per-tile base plus
     // this lane's fixed 32-bit offset plus a uniform per-(i, r) offset, so the
     // accesses need no bounds checks and no per-element 64-bit index
-    // arithmetic.  (The fp32 accumulate here writes out0 only.)
-    const bool fast = m0 + BM <= pM && n0 + (p.swiglu ? BN / 2 : BN) <= pN;
-    char* const ob = static_cast<char*>(e.out0) + (m0 * e.ld0 + n0) * ESO;   // output tile base
-    const int64_t old = e.ld0;                                               // its leading dimension
+    // arithmetic.  The fp32 accumulate splits its columns at nsplit (columns
+    // n >= nsplit go to out1 at n - nsplit): a tile on one side takes that
+    // side's base, a tile across the split goes the edge way.
+    const bool hi_side = EPI == EPI_ACC_F32 && n0 >= e.nsplit;
+    const bool straddle = EPI == EPI_ACC_F32 && n0 < e.nsplit && n0 + BN > e.nsplit;
+    const bool fast = m0 + BM <= pM && n0 + (p.swiglu ? BN / 2 : BN) <= pN && !straddle;
+    char* const ob = hi_side ? static_cast<char*>(e.out1) + (m0 * e.ld1 + n0 - e.nsplit) * ESO
+                             : static_cast<char*>(e.out0) + (m0 * e.ld0 + n0) * ESO;   // output tile base
+    const int64_t old = hi_side ? e.ld1 : e.ld0;                                      // its leading dimension
 
     const uint32_t lo = (uint32_t)(((int64_t)lr * old + lc) * ESO);
     const uint32_t li = (uint32_t)(((int64_t)lr * e.ldi0 + lc) * 2);
@@ -480,6 +485,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
         EpiPtr a{};
         a.o0 = static_cast<char*>(e.out0) + (row * e.ld0 + col) * ESO;
         if constexpr (EPI == EPI_ACC_F32) {
+            if (col >= e.nsplit) a.o0 = static_cast<char*>(e.out1) + (row * e.ld1 + col - e.nsplit) * ESO;
             a.i0 = a.o0;
         } else {
             if constexpr (EPI == EPI_SWIGLU) {
@@ -625,11 +631,14 @@ hipError_t launch(const Params& p, hipStream_t s) {
 
 int64_t swiglu_b_rows(int64_t ffn) { return 2 * ((ffn + 31) / 32) * 32; }
 
+int64_t gemm_bf16_tiles(int64_t M, int64_t N) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+
 // Requires A and B K-contiguous, every operand extent under 2 GB, N, the
 // output and input leading dimensions and the SwiGLU-backward split column
 // multiples of 8 and the epilogue pointers 16-byte aligned (the epilogue
 // moves 8 consecutive output columns, SwiGLU 4 hidden columns, per 16-byte
-// access); the fp32 accumulate writes out0 only (nsplit >= N).  With the
+// access); the fp32 accumulate's split column nsplit and out1's leading
+// dimension are multiples of 8 when nsplit < N.  With the
 // SwiGLU map, B is the gate/up weight interleaved per 32 hidden columns (32
 // gate rows, then 32 up rows; swiglu_b_rows(N) rows) and N is the number of
 // hidden columns.
@@ -638,7 +647,8 @@ hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
     const bool in = a.epi == EPI_RESID || a.epi == EPI_SWIGLU_BWD;
     if (a.N % 8 || a.e.ld0 % 8 || (in && a.e.ldi0 % 8) || (a.epi == EPI_SWIGLU_BWD && a.e.nsplit % 8))
         return hipErrorInvalidValue;
-    if (a.epi == EPI_ACC_F32 && a.e.nsplit < a.N) return hipErrorInvalidValue;
+    if (a.epi == EPI_ACC_F32 && a.e.nsplit < a.N && (!a.e.out1 || a.e.nsplit % 8 || a.e.ld1 % 8))
+        return hipErrorInvalidValue;
     if (a.epi == EPI_SWIGLU_BWD && (a.e.out2 || a.e.out3) && (a.M % BM || a.N % BN || a.e.ld2 < a.M || a.e.ld2 % 8))
         return hipErrorInvalidValue;   // h, dg, du are written transposed from full tiles only
     if (a.e.out3 && a.epi != EPI_SWIGLU_BWD) return hipErrorInvalidValue;

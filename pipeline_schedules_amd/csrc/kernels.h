@@ -24,7 +24,7 @@ enum Epi {
                          // and if out2: h = silu(g) u at out2[m*ldi0+n] (fp32 GEMM) or
                          // out2[n*ld2+m] (bf16 GEMM; with out3 also dg, du transposed)
     EPI_ACC_F32 = 4,     // n <  nsplit: out0[m*ld0+n] += acc; else out1[m*ld1+n-nsplit] += acc
-                         // (bf16: out0 only, nsplit >= N)
+                         // (bf16: nsplit and ld1 multiples of 8)
     EPI_BIAS_GELU = 5,   // z = acc + bias[n]; out0 = z, out1 = GELU(z)   (fp32 only)
     EPI_STORE = 6,       // out0[m*ld0+n] = acc                           (storage type)
 };
@@ -109,6 +109,10 @@ hipError_t transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t l
 
 // Rows of the interleaved gate/up weight copy used by the forward GEMM.
 int64_t swiglu_b_rows(int64_t ffn);
+
+// Workgroups (256 x 256 output tiles, one per CU at a time) of a bf16 GEMM
+// with M x N outputs.
+int64_t gemm_bf16_tiles(int64_t M, int64_t N);
 
 // dst = src * scale (n elements of the storage type)
 hipError_t scale(int dtype, void* dst, const void* src, int64_t n, float scale, hipStream_t s);

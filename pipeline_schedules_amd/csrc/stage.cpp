@@ -81,6 +81,7 @@ struct pps_stage {
     size_t s_hT = 0, s_nT = 0, s_dyT = 0, s_dguT = 0;
     int64_t Tp = 0;
     bool tn = false;                  // bf16 path: the forward GEMMs read K-contiguous weight copies
+    int ncu = 256;                    // compute units of the handle's device (GEMM tile waves)
     // bf16 path: per-pass copies of the forward weights, [chunk*L + block]:
     // WguT (swiglu_b_rows(ffn) x d, gate/up interleaved per 32) and WdT (d x ffn)
     char* wcopy = nullptr;
@@ -413,18 +414,24 @@ int swiglu_weight(pps_stage* h, int slot, int chunk, int b, const void* dy, cons
     a.e.out0 = dWd; a.e.ld0 = d; a.e.nsplit = d;
     PPS_TRY(timed(h, PPS_K_WGRAD_DOWN, gemm_flops(f, d, T), 0.0, [&] { return pps::gemm(dt, a, h->stream); }));
     c.epi = pps::EPI_ACC_F32;
-    if (h->tn) {
-        // the K-contiguous kernel accumulates into one output: dW_g, then dW_u
-        // from the second half of dg|du's rows
-        c.N = f;
-        c.e.out0 = dWg; c.e.ld0 = f; c.e.nsplit = f;
-        PPS_TRY(timed(h, PPS_K_WGRAD_GATEUP, gemm_flops(d, f, T), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
-        c.seg[0].B = static_cast<const char*>(c.seg[0].B) + (size_t)f * h->Tp * 2;
-        c.e.out0 = dWu;
-        PPS_TRY(timed(h, PPS_K_WGRAD_GATEUP, gemm_flops(d, f, T), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
-        return PPS_OK;
-    }
     c.e.out0 = dWg; c.e.ld0 = f; c.e.out1 = dWu; c.e.ld1 = f; c.e.nsplit = f;
+    if (h->tn) {
+        // bf16: dW_g and dW_u in one launch over the 2 ffn columns of dg|du
+        // (split at ffn) when that saves a partly filled wave of tiles (one
+        // tile per CU at a time), else one launch each: with whole waves
+        // either way, two launches measured faster.
+        const int64_t t1 = pps::gemm_bf16_tiles(d, f), t2 = pps::gemm_bf16_tiles(d, 2 * f);
+        auto waves = [&](int64_t t) { return (t + h->ncu - 1) / h->ncu; };
+        if (waves(t2) >= 2 * waves(t1)) {
+            c.N = f;
+            c.e.out1 = nullptr; c.e.ld1 = 0;
+            PPS_TRY(timed(h, PPS_K_WGRAD_GATEUP, gemm_flops(d, f, T), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
+            c.seg[0].B = static_cast<const char*>(c.seg[0].B) + (size_t)f * h->Tp * 2;
+            c.e.out0 = dWu;
+            PPS_TRY(timed(h, PPS_K_WGRAD_GATEUP, gemm_flops(d, f, T), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
+            return PPS_OK;
+        }
+    }
     PPS_TRY(timed(h, PPS_K_WGRAD_GATEUP, gemm_flops(d, 2.0 * f, T), 0.0, [&] { return pps::gemm(dt, c, h->stream); }));
     return PPS_OK;
 }
@@ -738,6 +745,14 @@ int create_stage(const pps_stage_desc* desc, pps_stage** out, bool noalloc) {
         h->wcopy = h->wcopy_bytes ? base + o : nullptr;
     }
     if (!h->bookkeeping) {
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            ncu < 1) {
+            (void)hipGetLastError();
+            release(h);
+            return PPS_EHIP;
+        }
+        h->ncu = ncu;
         if (!noalloc &&
             (hipMalloc(reinterpret_cast<void**>(&h->pool), pool_alloc) != hipSuccess ||
              hipMalloc(reinterpret_cast<void**>(&h->scratch), h->scratch_bytes) != hipSuccess ||
