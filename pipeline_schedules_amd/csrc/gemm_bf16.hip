@@ -37,8 +37,8 @@
 //
 // Workgroup -> tile mapping: the dispatcher places workgroup i on XCD i % 8;
 // ids are remapped so each XCD gets a contiguous run of logical tiles, and
-// logical tiles are ordered in groups of 8 tile-rows so the tiles running on
-// one XCD share A rows and B columns in that XCD's L2.
+// logical tiles are ordered in groups of 8 (or 4) tile-rows so the tiles
+// running on one XCD share A rows and B columns in that XCD's L2.
 #include <algorithm>
 #include <type_traits>
 
@@ -59,7 +59,6 @@ constexpr int ROWB = BK * 2;             // TN: 128 bytes per LDS row
 constexpr int OPB = 256 * ROWB;          // 32 KB per operand tile
 constexpr int NSLOT = 5;                 // operand-tile slots
 constexpr int LDS_BYTES = NSLOT * OPB;   // 160 KB
-constexpr int GROUP_M = 8;
 constexpr uint32_t OOB = 0x80000000u;    // an offset past every operand extent
 
 struct Seg {
@@ -72,6 +71,7 @@ struct Seg {
 struct Params {
     int64_t M, N, NB;      // NB = rows of B
     int tiles_m, tiles_n, nseg, swiglu;
+    int group_m;           // tile rows per group of the workgroup order (4 or 8)
     Seg seg[2];
     EpiArgs e;
 };
@@ -86,9 +86,9 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
     const int tall = (nwg & 7) ? (nwg & 7) : 8;
     const int xcd = bid & 7, local = bid >> 3;
     const int lin = xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
-    const int width = GROUP_M * p.tiles_n;
-    const int first_m = (lin / width) * GROUP_M;
-    const int gsize = min(p.tiles_m - first_m, GROUP_M);
+    const int width = p.group_m * p.tiles_n;
+    const int first_m = (lin / width) * p.group_m;
+    const int gsize = min(p.tiles_m - first_m, p.group_m);
     const int in = lin % width;
     tm = first_m + in % gsize;
     tn = in / gsize;
@@ -666,6 +666,13 @@ hipError_t gemm_bf16(const GemmArgs& a, hipStream_t s) {
     p.tiles_m = (int)((a.M + BM - 1) / BM);
     p.tiles_n = (int)((a.N + cols_per_tile - 1) / cols_per_tile);
     p.NB = a.swiglu_map ? swiglu_b_rows(a.N) : a.N;
+    // The 32 tiles an XCD runs at once span group_m tile rows x 32/group_m
+    // tile columns: 8 x 4 fetches each B panel slice for 8 tiles and each A
+    // slice for 4, 4 x 8 the other way round.  With more than twice as many
+    // A rows as B rows (weight gradient of W_d: A = h^T, B = dy^T) A is the
+    // operand that does not stay in the on-package cache, so its panels are
+    // the ones to share; the SwiGLU-backward role measured faster with 4 too.
+    p.group_m = (a.M > 2 * p.NB || a.epi == EPI_SWIGLU_BWD) ? 4 : 8;
     for (int i = 0; i < a.nseg; ++i) {
         const GemmSeg& g = a.seg[i];
         p.seg[i].A = static_cast<const uint16_t*>(g.A);
