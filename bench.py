@@ -58,6 +58,11 @@ def _measured_traffic(config_name, kernel_name):
     return TRAFFIC["bytes_per_launch"].get(kernel_name)
 
 
+def _sig(x):
+    """x to two decimals, or to four significant digits when that would round it to zero."""
+    return round(x, 2) if abs(x) >= 1.0 else float(f"{x:.4g}")
+
+
 def _log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -153,6 +158,32 @@ def vendor_reference(cfg, reps=10):
         torch.cuda.empty_cache()
     return {"library": "hipBLASLt via torch.mm / torch.addmm(out_dtype=float32)", "reps": reps,
             "addmm_fp32_check_rel_l2": check, "gemms": out}
+
+
+def pipeline_model_from_times(cfg, kernels):
+    """The P-stage timeline this stage's measured per-op times imply (no
+    transfer time): every stage is assumed to cost what this one does.
+    ``kernels`` maps kernel-role names to {"total_ms_per_step": ...}."""
+    from pipeline_schedules_amd import pps
+    per_mb = lambda names: sum(kernels[n]["total_ms_per_step"] for n in names if n in kernels) / cfg.M
+    t_f = per_mb(["rmsnorm_fwd", "gemm_gateup_swiglu", "gemm_down_residual"])
+    t_bx = per_mb(["gemm_dh_swiglu_bwd", "gemm_dn", "rmsnorm_bwd_residual", "dgamma_reduce"])
+    # "copy" also holds the once-per-pass weight refresh; it is charged to W
+    t_w = per_mb(["prep_w", "gemm_wgrad_down", "gemm_wgrad_gateup", "copy"])
+    model = {"P": cfg.P, "M": cfg.M, "t_f_ms": round(t_f, 3), "t_b_ms": round(t_bx + t_w, 3),
+             "t_b_input_ms": round(t_bx, 3), "t_w_ms": round(t_w, 3), "transfer_ms": 0.0}
+    for name, kind, v, tf, tb, tw in (("gpipe", pps.GPIPE, 1, t_f, t_bx + t_w, 0.0),
+                                      ("1f1b", pps.ONE_F_ONE_B, 1, t_f, t_bx + t_w, 0.0),
+                                      ("interleaved_v2", pps.ONE_F_ONE_B, 2, t_f / 2, (t_bx + t_w) / 2, 0.0),
+                                      ("zb1p", pps.ZB1P, 1, t_f, t_bx, t_w),
+                                      ("zb2p", pps.ZB2P, 1, t_f, t_bx, t_w)):
+        if v > 1 and cfg.M % cfg.P:
+            # the interleaved order takes micro-batches in groups of P
+            model[name] = {"not_applicable": f"M = {cfg.M} is not a multiple of P = {cfg.P}"}
+            continue
+        mk, bubble = pps.simulate_pipeline(cfg.P, cfg.M, v, kind, tf, tb, tw)
+        model[name] = {"step_ms": round(mk, 1), "bubble": round(bubble, 4)}
+    return model
 
 
 def main():
@@ -289,7 +320,9 @@ def main():
         dom = max(kt, key=lambda k: k["total_ms"])
         if dom["flops"]:
             ach = dom["flops"] / (dom["total_ms"] * 1e-3) / 1e12
-            roofline = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+            # bf16 GEMMs run on the matrix cores; the fp32 path on the vector ALUs
+            roofline = {"bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": _sig(ach), "peak": peak,
+                        "unit": "TFLOP/s",
                         "frac": round(ach / peak, 4), "traffic": _measured_traffic(cfg.name, dom["name"]),
                         "kernel": dom["name"], "avg_launch_ms": dom["total_ms"] / dom["launches"],
                         "flops_per_launch": dom["flops"] / dom["launches"]}
@@ -300,24 +333,9 @@ def main():
                         "avg_launch_ms": dom["total_ms"] / dom["launches"],
                         "bytes_per_launch": dom["bytes"] / dom["launches"]}
 
-    # The P-stage timeline this stage's measured per-op times imply (no
-    # transfer time): every stage is assumed to cost what this one does.
     pipeline_model = None
     if kernels and cfg.block == "swiglu" and cfg.v == 1 and not args.recompute:
-        per_mb = lambda names: sum(kernels[n]["total_ms_per_step"] for n in names if n in kernels) / cfg.M
-        t_f = per_mb(["rmsnorm_fwd", "gemm_gateup_swiglu", "gemm_down_residual"])
-        t_bx = per_mb(["gemm_dh_swiglu_bwd", "gemm_dn", "rmsnorm_bwd_residual", "dgamma_reduce"])
-        # "copy" also holds the once-per-pass weight refresh; it is charged to W
-        t_w = per_mb(["prep_w", "gemm_wgrad_down", "gemm_wgrad_gateup", "copy"])
-        pipeline_model = {"P": cfg.P, "M": cfg.M, "t_f_ms": round(t_f, 3), "t_b_ms": round(t_bx + t_w, 3),
-                          "t_b_input_ms": round(t_bx, 3), "t_w_ms": round(t_w, 3), "transfer_ms": 0.0}
-        for name, kind, v, tf, tb, tw in (("gpipe", pps.GPIPE, 1, t_f, t_bx + t_w, 0.0),
-                                          ("1f1b", pps.ONE_F_ONE_B, 1, t_f, t_bx + t_w, 0.0),
-                                          ("interleaved_v2", pps.ONE_F_ONE_B, 2, t_f / 2, (t_bx + t_w) / 2, 0.0),
-                                          ("zb1p", pps.ZB1P, 1, t_f, t_bx, t_w),
-                                          ("zb2p", pps.ZB2P, 1, t_f, t_bx, t_w)):
-            mk, bubble = pps.simulate_pipeline(cfg.P, cfg.M, v, kind, tf, tb, tw)
-            pipeline_model[name] = {"step_ms": round(mk, 1), "bubble": round(bubble, 4)}
+        pipeline_model = pipeline_model_from_times(cfg, kernels)
 
     cpu = None
     if not args.no_cpu_baseline and cfg.block == "swiglu":
@@ -327,7 +345,7 @@ def main():
 
     out = {
         "metric": "stage F+B TFLOP/s & MFMA-peak fraction at P=8 slice; peak stash bytes",
-        "value": round(tflops, 2),
+        "value": _sig(tflops),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -339,8 +357,10 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: stage k={cfg.k} of P={cfg.P}, M={cfg.M} micro-batches, "
-                               f"{cfg.kind}{' v=' + str(cfg.v) if cfg.v > 1 else ''}, {cfg.L * cfg.v} SwiGLU blocks "
-                               f"d={cfg.d} ffn={cfg.f}, {cfg.T} tokens/micro-batch",
+                               f"{cfg.kind}{' v=' + str(cfg.v) if cfg.v > 1 else ''}, {cfg.L * cfg.v} "
+                               + (f"SwiGLU blocks d={cfg.d} ffn={cfg.f}" if cfg.block == "swiglu"
+                                  else f"Linear+GELU blocks d={cfg.d}")
+                               + f", {cfg.T} tokens/micro-batch",
                    "P": cfg.P, "M": cfg.M, "k": cfg.k, "v": cfg.v, "schedule": cfg.kind, "blocks": cfg.L * cfg.v,
                    "d": cfg.d, "ffn": cfg.f, "tokens_per_microbatch": cfg.T, "ops_per_step": len(ops),
                    "recompute": bool(args.recompute)},
@@ -350,7 +370,7 @@ def main():
         "stash_bound_entries": max(o[4] for o in ops),
         "flops_per_step": flops_per_pass,
         "executed_flops_per_step": flops_per_pass + extra,
-        "executed_tflops": round(executed_tflops, 2),
+        "executed_tflops": _sig(executed_tflops),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "pipeline_model": pipeline_model,
