@@ -194,7 +194,9 @@ typedef struct pps_stage pps_stage;
  * Nothing is allocated later.
  * Limits: P, M, v, L >= 1, 0 <= k < P, kind one of the PPS_* kinds,
  * P*v*M <= 2^24, v*L <= 2^20 (checked before anything is allocated);
- * d a multiple of 8 up to 16384, ffn a multiple of 8; with bf16 SwiGLU
+ * d a multiple of 8 up to 16384, ffn a multiple of 8 up to 2^30, T up to
+ * 2^24 rows, and a memory footprint (pool, scratch, gradients, weight
+ * copies) that stays under 10^18 bytes; with bf16 SwiGLU
  * blocks every GEMM operand must stay under 2 GiB (T * 2ffn, T * d and
  * 2*ceil(ffn/32)*32 * d elements of 2 bytes, T rounded up to 8), since the
  * MFMA kernel addresses operands with 32-bit offsets.

@@ -249,7 +249,8 @@ int build_lists(int P, int M, int v, int kind, std::vector<std::vector<Op3>>& li
                 std::vector<std::vector<int>>& start, bool& split) {
     if (P < 1 || M < 1 || v < 1) return PPS_EINVAL;
     if (kind < PPS_GPIPE || kind > PPS_ZB2P) return PPS_EINVAL;
-    if ((long long)P * v * M > (1LL << 24)) return PPS_EINVAL;
+    // P*v first: with it bounded the product with M cannot overflow
+    if ((long long)P * v > (1LL << 24) || (long long)P * v * M > (1LL << 24)) return PPS_EINVAL;
     if (v > 1 && (kind != PPS_1F1B || M % P != 0)) return PPS_EINVAL;
     lists.assign(P, {});
     split = false;

@@ -187,12 +187,29 @@ int validate_desc(const pps_stage_desc* d) {
     // Schedule parameters first: everything below sizes host arrays from them.
     if (d->P < 1 || d->M < 1 || d->v < 1 || d->L < 1 || d->k < 0 || d->k >= d->P) return PPS_EINVAL;
     if (d->kind < PPS_GPIPE || d->kind > PPS_ZB2P) return PPS_EINVAL;
-    if ((long long)d->P * d->v * d->M > (1LL << 24) || (long long)d->v * d->L > (1LL << 20)) return PPS_EINVAL;
+    if ((long long)d->P * d->v > (1LL << 24) || (long long)d->P * d->v * d->M > (1LL << 24) ||
+        (long long)d->v * d->L > (1LL << 20))
+        return PPS_EINVAL;
     if (d->block_type != PPS_BLOCK_SWIGLU && d->block_type != PPS_BLOCK_TOY_GELU) return PPS_EINVAL;
     if (d->dtype != PPS_DTYPE_BF16 && d->dtype != PPS_DTYPE_FP32) return PPS_EINVAL;
     if (d->block_type == PPS_BLOCK_TOY_GELU && d->dtype != PPS_DTYPE_FP32) return PPS_EINVAL;
-    if (d->L < 1 || d->d < 8 || d->d % 8 != 0 || d->d > 16384 || d->T < 0) return PPS_EINVAL;
+    // T: the RMSNorm forward launches one workgroup of 256 lanes per row
+    if (d->L < 1 || d->d < 8 || d->d % 8 != 0 || d->d > 16384 || d->T < 0 || d->T > (1LL << 24)) return PPS_EINVAL;
     if (d->block_type == PPS_BLOCK_SWIGLU && (d->ffn < 8 || d->ffn % 8 != 0)) return PPS_EINVAL;
+    if (d->block_type == PPS_BLOCK_SWIGLU && d->ffn > (1LL << 30)) return PPS_EINVAL;
+    {
+        // Every byte count the layout forms (stash slots, scratch, gradients,
+        // weight copies) stays far inside 64 bits: bound the whole footprint
+        // from above in double precision, 4-byte elements and generous
+        // padding throughout.
+        const double T = (double)d->T, dm = (double)d->d, f = d->block_type == PPS_BLOCK_SWIGLU ? (double)d->ffn : dm;
+        const double blocks = (double)d->v * d->L, pad = 64.0 * 256.0;
+        const double tensors = (T + 8) * (2.0 * dm + 4.0 * f + 2.0) * 4.0 + pad;   // one block's entry (+ split)
+        const double pool = (double)d->M * d->v * (d->L * tensors + pad);
+        const double scratch = (T + 8) * (8.0 * dm + 8.0 * f + 8.0) * 4.0 + pad;
+        const double params = blocks * ((3.0 * dm * f + dm * dm + dm) * 4.0 + (2.0 * (f + 32) * dm + dm * f) * 2.0 + pad);
+        if (pool + tensors * d->L + scratch + params > 1e18) return PPS_EINVAL;
+    }
     if ((d->flags & PPS_FLAG_RECOMPUTE) &&
         (d->block_type != PPS_BLOCK_SWIGLU || d->kind == PPS_ZB1P || d->kind == PPS_ZB2P))
         return PPS_EINVAL;
@@ -220,23 +237,31 @@ int validate_desc(const pps_stage_desc* d) {
 void release(pps_stage* h) {
     if (!h) return;
     for (hipEvent_t e : h->ev)
-        if (e) hipEventDestroy(e);
+        if (e) (void)hipEventDestroy(e);
     if (!h->noalloc) {
-        if (h->pool) hipFree(h->pool);
-        if (h->scratch) hipFree(h->scratch);
-        if (h->grads) hipFree(h->grads);
-        if (h->wcopy) hipFree(h->wcopy);
+        if (h->pool) (void)hipFree(h->pool);
+        if (h->scratch) (void)hipFree(h->scratch);
+        if (h->grads) (void)hipFree(h->grads);
+        if (h->wcopy) (void)hipFree(h->wcopy);
     }
     delete h;
 }
 
+bool pass_done(const pps_stage* h) {
+    return h->fpos == h->fseq.size() && h->bpos == h->bseq.size() && h->wpos == h->wseq.size();
+}
+
 void maybe_new_pass(pps_stage* h) {
-    if (h->fpos == h->fseq.size() && h->bpos == h->bseq.size() && h->wpos == h->wseq.size()) {
+    if (pass_done(h)) {
         h->fpos = h->bpos = h->wpos = 0;
         std::fill(h->status.begin(), h->status.end(), ST_NONE);
         h->oplog.clear();
-        ++h->st.passes_completed;
     }
+}
+
+// After an accepted op: the op that completes the op list completes a pass.
+void count_pass(pps_stage* h) {
+    if (pass_done(h)) ++h->st.passes_completed;
 }
 
 void log_op(pps_stage* h, int op, int mb, int chunk, int slot, int t) {
@@ -810,7 +835,7 @@ extern "C" int pps_stage_forward(pps_stage* h, int mb, int chunk, const void* x_
     if (mb < 0 || mb >= h->d.M || chunk < 0 || chunk >= h->d.v) return PPS_EINVAL;
     if (!h->bookkeeping && (!x_in || !y_out || !aligned16(x_in) || !aligned16(y_out))) return PPS_EINVAL;
     // A call after a completed pass starts the next one.
-    const bool next_pass = h->fpos == h->fseq.size() && h->bpos == h->bseq.size() && h->wpos == h->wseq.size();
+    const bool next_pass = pass_done(h);
     const size_t fpos = next_pass ? 0 : h->fpos;
     if (fpos >= h->fseq.size() || h->fseq[fpos] != std::make_pair(mb, chunk)) return PPS_EORDER;
     int slot = 0;
@@ -835,6 +860,7 @@ extern "C" int pps_stage_forward(pps_stage* h, int mb, int chunk, const void* x_
     log_op(h, PPS_OP_F, mb, chunk, slot, h->tf[h->fpos]);
     ++h->fpos;
     ++h->st.n_forward;
+    count_pass(h);
     return PPS_OK;
 }
 
@@ -852,8 +878,7 @@ extern "C" int pps_stage_backward(pps_stage* h, int mb, int chunk, const void* d
     }
     const size_t key = (size_t)chunk * h->d.M + mb;
     // after a completed pass nothing of the next one is saved yet
-    const bool pass_done = h->fpos == h->fseq.size() && h->bpos == h->bseq.size() && h->wpos == h->wseq.size();
-    if (pass_done || h->status[key] == ST_NONE) return PPS_ENOENT;
+    if (pass_done(h) || h->status[key] == ST_NONE) return PPS_ENOENT;
     if (h->status[key] != ST_F) return PPS_ESTATE;
     if (h->bpos >= h->bseq.size() || h->bseq[h->bpos] != std::make_pair(mb, chunk)) return PPS_EORDER;
     const int slot = h->slot_of[key];
@@ -874,6 +899,7 @@ extern "C" int pps_stage_backward(pps_stage* h, int mb, int chunk, const void* d
     log_op(h, PPS_OP_B, mb, chunk, slot, h->tb[h->bpos]);
     ++h->bpos;
     ++h->st.n_backward;
+    count_pass(h);
     return PPS_OK;
 }
 
@@ -897,6 +923,7 @@ extern "C" int pps_stage_backward_weight(pps_stage* h, int mb, int chunk) {
     log_op(h, PPS_OP_W, mb, chunk, slot, h->tw[h->wpos]);
     ++h->wpos;
     ++h->st.n_backward_weight;
+    count_pass(h);
     return PPS_OK;
 }
 

@@ -132,7 +132,7 @@ def test_bookkeeping_oplog_matches_oracle(kind, v):
                 assert s["n_slots"] == peak
                 assert s["peak_live_entries"] == peak
                 assert s["live_entries"] == 0 and s["live_bytes"] == 0
-                assert s["passes_completed"] == 1
+                assert s["passes_completed"] == 2
                 st.close()
 
 

@@ -551,5 +551,5 @@ def test_pass_repeats_and_zero_grad(env):
     st.zero_grad()
     z = G.stage_grads(st, 1, "swiglu", cfg.d, cfg.f)
     assert all(not v.any() for v in z[0].values())
-    assert st.stats()["passes_completed"] == 1
+    assert st.stats()["passes_completed"] == 2
     st.close()
