@@ -5,7 +5,9 @@ a dtype and token/feature sizes that mix ragged and whole 256-wide tiles,
 plus sometimes the recompute mode, then checks the op log against the
 oracle's schedule exactly and every output, input gradient and weight
 gradient against the oracle's full-batch step (rel-L2 <= 2e-2 bf16,
-<= 1e-5 fp32)."""
+<= 1e-5 fp32).  A second set of draws interleaves calls that cannot be valid
+with the schedule's ops and checks that they leave no trace (bit-identical
+results to a clean run)."""
 
 import numpy as np
 import pytest
@@ -66,3 +68,96 @@ def test_random_stage(env, case):
     peak = max(o[4] for o in S.stage_ops(cfg.P, cfg.M, cfg.k, 1, {"1f1b": S.ONE_F_ONE_B, "gpipe": S.GPIPE,
                                                                    "zb1p": S.ZB1P, "zb2p": S.ZB2P}[c["kind"]]))
     assert got[3]["peak_live_entries"] == peak
+
+
+def _bad_call(rng, M, split, nxt, fdone, bdone, wdone):
+    """A call that no state of the pass can accept here: (op, mb, buffer role)
+    with role 'ok' (the right buffers), 'misaligned' or 'overlap'.  ``nxt`` is
+    the schedule's next op (op, mb)."""
+    for _ in range(32):
+        kind = int(rng.integers(0, 6))
+        if kind == 0:
+            return int(rng.integers(0, 3)), int(rng.choice([-1, M])), "ok"
+        if kind == 1 and fdone:
+            return 0, sorted(fdone)[int(rng.integers(0, len(fdone)))], "ok"        # forward again
+        if kind == 2:
+            pool = [m for m in range(M) if m not in fdone or m in bdone]
+            if pool:
+                return 1, pool[int(rng.integers(0, len(pool)))], "ok"            # no entry, or twice
+        if kind == 3:
+            pool = list(range(M)) if not split else [m for m in range(M) if m not in bdone or m in wdone]
+            if pool:
+                return 2, pool[int(rng.integers(0, len(pool)))], "ok"            # W without the split / early
+        if kind == 4 and nxt[0] in (0, 1):
+            return nxt[0], nxt[1], "misaligned"
+        if kind == 5 and nxt[0] == 1:
+            return 1, nxt[1], "overlap"
+    return 0, -1, "ok"
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_rejected_calls_leave_no_trace(env, case):
+    # Between the schedule's ops, calls that cannot be valid at that point
+    # (micro-batches out of range, repeated or premature; W without the split
+    # or before its B; misaligned or overlapping buffers for the next op)
+    # return an error status and enqueue nothing: the pass then gives the bits
+    # of a clean run and the op log holds only the schedule.
+    from pipeline_schedules_amd.configs import StageConfig
+    from pipeline_schedules_amd.inputs import make_inputs
+    from tests.test_gpu_stage import _run_single
+    torch, pps, G = env
+    c = _draw(1000 + case)
+    c["kind"] = ["1f1b", "gpipe", "zb1p", "zb2p"][case % 4]
+    c["recompute"] = c["recompute"] and c["kind"] in ("1f1b", "gpipe")
+    print(c, flush=True)
+    cfg = StageConfig(f"rejected{case}", P=c["P"], M=c["M"], k=c["k"], v=1, kind=c["kind"], block="swiglu",
+                      dtype=c["dtype"], L=c["L"], d=c["d"], f=c["f"], T=c["T"])
+    inp = make_inputs(cfg, gamma="random")
+    flags = pps.FLAG_RECOMPUTE if c["recompute"] else 0
+    ref = _run_single(env, cfg, inp, c["kind"], flags=flags)
+    w = G.upload_params(inp.params[0], "swiglu", cfg.dtype)
+    st = pps.stage_from_config(cfg, weights=w, kind=c["kind"], stream=torch.cuda.current_stream(), flags=flags)
+    ops = pps.make_schedule(cfg.P, cfg.M, cfg.k, 1, pps.KIND_BY_NAME[c["kind"]])
+    td = G.tdtype(cfg.dtype)
+    xs = [G.to_dev(x, cfg.dtype) for x in inp.xs]
+    dys = [G.to_dev(g, cfg.dtype) for g in inp.Gs]
+    ys = [torch.empty((cfg.T, cfg.d), dtype=td, device="cuda") for _ in range(cfg.M)]
+    dxs = [torch.empty((cfg.T, cfg.d), dtype=td, device="cuda") for _ in range(cfg.M)]
+    spare = torch.empty(cfg.T * cfg.d + 16, dtype=td, device="cuda")
+    mis = spare.data_ptr() + 2
+    rng = np.random.default_rng(4242 + case)
+    split = c["kind"] in ("zb1p", "zb2p")
+    fdone, bdone, wdone = set(), set(), set()
+    rejected = 0
+    for op, mb, ch, *_ in ops:
+        for _ in range(int(rng.integers(0, 3))):
+            bop, bmb, role = _bad_call(rng, cfg.M, split, (op, mb), fdone, bdone, wdone)
+            i = min(max(bmb, 0), cfg.M - 1)   # buffers of an in-range micro-batch
+            if bop == 0:
+                rc = st.forward_status(bmb, 0, mis if role == "misaligned" else xs[i], ys[i])
+            elif bop == 1:
+                dy = mis if role == "misaligned" else dxs[i] if role == "overlap" else dys[i]
+                rc = st.backward_status(bmb, 0, dy, dxs[i])
+            else:
+                rc = st.backward_weight_status(bmb, 0)
+            assert rc < 0, (bop, bmb, role, rc)
+            rejected += 1
+        if op == pps.OP_F:
+            st.forward(mb, ch, xs[mb], ys[mb])
+            fdone.add(mb)
+        elif op == pps.OP_B:
+            st.backward(mb, ch, dys[mb], dxs[mb])
+            bdone.add(mb)
+        else:
+            st.backward_weight(mb, ch)
+            wdone.add(mb)
+    st.sync()
+    print("rejected calls:", rejected, flush=True)
+    assert st.oplog() == ops
+    grads = G.stage_grads(st, cfg.L, "swiglu", cfg.d, cfg.f)
+    for i in range(cfg.M):
+        assert np.array_equal(G.to_host(ys[i]), ref[0][i]) and np.array_equal(G.to_host(dxs[i]), ref[1][i]), i
+    for blk in range(cfg.L):
+        for key in ref[2][blk]:
+            assert np.array_equal(grads[blk][key], ref[2][blk][key]), (blk, key)
+    st.close()
