@@ -145,7 +145,8 @@ int pps_simulate_pipeline(int P, int M, int v, int kind, double t_f, double t_b,
 #define PPS_FLAG_BOOKKEEPING_ONLY 1u /* validate calls and track the stash and
                                         op log only: no device memory, no
                                         kernels, pointers are not touched     */
-#define PPS_FLAG_PROFILE          2u /* record HIP events around each kernel  */
+#define PPS_FLAG_PROFILE          2u /* record HIP events around kernels (see
+                                        profile_stride)                       */
 /* Activation recompute ([GPipe→ZB "GPipe 2018年"]: keep only the stage
    boundary and redo each layer's forward when the backward reaches it;
    [1F1B §4.5]: still advised under 1F1B).  A stash entry is then the stage
@@ -169,7 +170,9 @@ typedef struct pps_stage_desc {
     float   eps;                /* RMSNorm epsilon                           */
     uint32_t flags;             /* PPS_FLAG_*                                */
     int32_t profile_capacity;   /* max kernel launches timed (PROFILE only)  */
-    int32_t reserved;
+    int32_t profile_stride;     /* PROFILE only: time launches 0, s, 2s, ... of
+                                   each kernel id (0 or 1: every launch); the
+                                   events cost GPU time between kernels      */
     void*   stream;             /* hipStream_t; NULL = the null stream        */
     /* Caller-owned device weights, read-only, must outlive the handle and
        stay unchanged during a pass (first forward to last backward or W:
@@ -323,15 +326,19 @@ int pps_stage_get_oplog(const pps_stage* h, pps_op* ops, int cap, int* n);
 typedef struct pps_kernel_time {
     int32_t kernel;      /* PPS_K_*                                          */
     int32_t reserved;
-    int64_t launches;    /* timed launches                                   */
-    double  total_ms;    /* sum of HIP-event durations                       */
-    double  flops;       /* algorithmic FLOPs summed over the launches        */
-    double  bytes;       /* algorithmic HBM bytes summed over the launches    */
+    int64_t launches;    /* launches since the previous call                 */
+    int64_t timed;       /* of which timed (see profile_stride); may be 0    */
+    double  total_ms;    /* sum of the timed launches' HIP-event durations   */
+    double  flops;       /* algorithmic FLOPs summed over the timed launches */
+    double  bytes;       /* algorithmic HBM bytes summed over the timed ones */
 } pps_kernel_time;
 
 /* Synchronizes the stream, folds the recorded event pairs into per-kernel
-   totals, writes one entry per kernel id that has launches, and resets the
-   recorder.  PPS_EINVAL without PPS_FLAG_PROFILE. */
+   totals, writes one entry per kernel id launched since the previous call,
+   and resets the totals (the stride's phase carries on).  Average duration
+   = total_ms / timed.  Launches past profile_capacity timed pairs since the
+   previous call are counted, not timed.  PPS_EINVAL without
+   PPS_FLAG_PROFILE. */
 int pps_stage_kernel_times(pps_stage* h, pps_kernel_time* out, int cap, int* n);
 const char* pps_kernel_name(int kernel);
 

@@ -99,7 +99,10 @@ struct pps_stage {
     double kt_ms[PPS_K_COUNT] = {};
     double kt_flops[PPS_K_COUNT] = {};
     double kt_bytes[PPS_K_COUNT] = {};
-    int64_t kt_n[PPS_K_COUNT] = {};
+    int64_t kt_n[PPS_K_COUNT] = {};       // timed launches since the last report
+    int64_t kt_calls[PPS_K_COUNT] = {};   // all launches since the last report
+    int64_t kt_seen[PPS_K_COUNT] = {};    // all launches since create (the stride's phase)
+    int stride = 1;
 };
 
 namespace {
@@ -119,7 +122,11 @@ char* act_x(pps_stage* h, int slot, int b) {
 
 template <typename F>
 hipError_t timed(pps_stage* h, int kernel, double flops, double bytes, F&& launch) {
-    const bool rec = h->profile && h->ev_used < (int)h->ev_kernel.size();
+    bool rec = false;
+    if (h->profile) {
+        rec = h->kt_seen[kernel]++ % h->stride == 0 && h->ev_used < (int)h->ev_kernel.size();
+        ++h->kt_calls[kernel];
+    }
     if (rec) {
         hipError_t e = hipEventRecord(h->ev[2 * h->ev_used], h->stream);
         if (e != hipSuccess) return e;
@@ -224,7 +231,7 @@ int validate_desc(const pps_stage_desc* d) {
         if (Tp * f2 * 2 >= lim || Tp * (double)d->d * 2 >= lim || rows * (double)d->d * 2 >= lim)
             return PPS_EINVAL;
     }
-    if ((d->flags & PPS_FLAG_PROFILE) && d->profile_capacity < 0) return PPS_EINVAL;
+    if ((d->flags & PPS_FLAG_PROFILE) && (d->profile_capacity < 0 || d->profile_stride < 0)) return PPS_EINVAL;
     if (!(d->flags & PPS_FLAG_BOOKKEEPING_ONLY)) {
         if (!d->weights) return PPS_EINVAL;
         const int nw = d->block_type == PPS_BLOCK_SWIGLU ? 4 : 2;
@@ -664,6 +671,7 @@ int create_stage(const pps_stage_desc* desc, pps_stage** out, bool noalloc) {
     h->d = *desc;
     h->bookkeeping = (desc->flags & PPS_FLAG_BOOKKEEPING_ONLY) != 0;
     h->profile = !h->bookkeeping && (desc->flags & PPS_FLAG_PROFILE) != 0;
+    h->stride = std::max(1, desc->profile_stride);
     h->swiglu = desc->block_type == PPS_BLOCK_SWIGLU;
     h->nw = h->swiglu ? 4 : 2;
     h->es = desc->dtype == PPS_DTYPE_BF16 ? 2 : 4;
@@ -982,20 +990,21 @@ extern "C" int pps_stage_kernel_times(pps_stage* h, pps_kernel_time* out, int ca
     h->ev_used = 0;
     int cnt = 0;
     for (int k = 0; k < PPS_K_COUNT; ++k)
-        if (h->kt_n[k]) ++cnt;
+        if (h->kt_calls[k]) ++cnt;
     *n = cnt;
     if (cap < cnt) return PPS_EFULL;
     int j = 0;
     for (int k = 0; k < PPS_K_COUNT; ++k) {
-        if (!h->kt_n[k]) continue;
+        if (!h->kt_calls[k]) continue;
         out[j].kernel = k;
         out[j].reserved = 0;
-        out[j].launches = h->kt_n[k];
+        out[j].launches = h->kt_calls[k];
+        out[j].timed = h->kt_n[k];
         out[j].total_ms = h->kt_ms[k];
         out[j].flops = h->kt_flops[k];
         out[j].bytes = h->kt_bytes[k];
         ++j;
-        h->kt_n[k] = 0;
+        h->kt_n[k] = h->kt_calls[k] = 0;
         h->kt_ms[k] = h->kt_flops[k] = h->kt_bytes[k] = 0.0;
     }
     return PPS_OK;

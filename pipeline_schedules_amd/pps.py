@@ -50,7 +50,7 @@ class PpsStageDesc(ctypes.Structure):
                 ("kind", ctypes.c_int32), ("block_type", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("L", ctypes.c_int32), ("d", ctypes.c_int64), ("ffn", ctypes.c_int64), ("T", ctypes.c_int64),
                 ("eps", ctypes.c_float), ("flags", ctypes.c_uint32), ("profile_capacity", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("stream", ctypes.c_void_p),
+                ("profile_stride", ctypes.c_int32), ("stream", ctypes.c_void_p),
                 ("weights", ctypes.POINTER(ctypes.c_void_p))]
 
 
@@ -66,7 +66,8 @@ class PpsStats(ctypes.Structure):
 
 class PpsKernelTime(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("reserved", ctypes.c_int32), ("launches", ctypes.c_int64),
-                ("total_ms", ctypes.c_double), ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
+                ("timed", ctypes.c_int64), ("total_ms", ctypes.c_double), ("flops", ctypes.c_double),
+                ("bytes", ctypes.c_double)]
 
 
 class PpsError(RuntimeError):
@@ -167,14 +168,14 @@ class Stage:
 
     def __init__(self, P, M, k, v=1, kind=ONE_F_ONE_B, block=BLOCK_SWIGLU, dtype=DTYPE_BF16, L=1,
                  d=64, ffn=64, T=8, eps=1e-6, weights=None, stream=None, flags=0, profile_capacity=0,
-                 noalloc=False):
+                 noalloc=False, profile_stride=0):
         self._h = None
         nw = 4 if block == BLOCK_SWIGLU else 2
         desc = PpsStageDesc()
         desc.P, desc.M, desc.k, desc.v, desc.kind = P, M, k, v, kind
         desc.block_type, desc.dtype, desc.L = block, dtype, L
         desc.d, desc.ffn, desc.T, desc.eps = d, ffn, T, eps
-        desc.flags, desc.profile_capacity = flags, profile_capacity
+        desc.flags, desc.profile_capacity, desc.profile_stride = flags, profile_capacity, profile_stride
         desc.stream = stream if isinstance(stream, int) or stream is None else stream.cuda_stream
         self._keep = weights
         if weights is not None:
@@ -268,7 +269,7 @@ class Stage:
         n = ctypes.c_int(0)
         _check(lib().pps_stage_kernel_times(self._h, arr, 32, ctypes.byref(n)), "pps_stage_kernel_times")
         return [{"kernel": arr[i].kernel, "name": kernel_name(arr[i].kernel), "launches": arr[i].launches,
-                 "total_ms": arr[i].total_ms, "flops": arr[i].flops, "bytes": arr[i].bytes}
+                 "timed": arr[i].timed, "total_ms": arr[i].total_ms, "flops": arr[i].flops, "bytes": arr[i].bytes}
                 for i in range(n.value)]
 
 
@@ -288,10 +289,10 @@ def _hip():
 
 
 def stage_from_config(cfg, weights=None, stream=None, flags=0, profile_capacity=0, k=None, T=None, M=None,
-                      kind=None, noalloc=False):
+                      kind=None, noalloc=False, profile_stride=0):
     """Stage handle for a ``configs.StageConfig`` (optionally overriding k, T, M, kind)."""
     return Stage(P=cfg.P, M=cfg.M if M is None else M, k=cfg.k if k is None else k, v=cfg.v,
                  kind=KIND_BY_NAME[cfg.kind if kind is None else kind], block=BLOCK_BY_NAME[cfg.block],
                  dtype=DTYPE_BY_NAME[cfg.dtype], L=cfg.L, d=cfg.d, ffn=cfg.f, T=cfg.T if T is None else T,
                  eps=cfg.eps, weights=weights, stream=stream, flags=flags, profile_capacity=profile_capacity,
-                 noalloc=noalloc)
+                 noalloc=noalloc, profile_stride=profile_stride)

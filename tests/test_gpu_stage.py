@@ -553,3 +553,36 @@ def test_pass_repeats_and_zero_grad(env):
     assert all(not v.any() for v in z[0].values())
     assert st.stats()["passes_completed"] == 2
     st.close()
+
+
+def test_profile_stride_times_every_nth_launch(env):
+    # PPS_FLAG_PROFILE with profile_stride 3: launches 0, 3, 6, ... of each
+    # kernel id carry HIP events; every launch is counted; the results are the
+    # bits of an unprofiled run.
+    torch, pps, G = env
+    from pipeline_schedules_amd.inputs import make_inputs
+    cfg = _swiglu_cfg("bf16", T=264, d=264, f=392, L=2, M=3, P=2)
+    inp = make_inputs(cfg, gamma="random")
+    ref = _run_single(env, cfg, inp, "1f1b")
+    w = G.upload_params(inp.params[0], "swiglu", "bf16")
+    st = pps.stage_from_config(cfg, weights=w, stream=torch.cuda.current_stream(), flags=pps.FLAG_PROFILE,
+                               profile_capacity=1000, profile_stride=3)
+    ops = pps.make_schedule(cfg.P, cfg.M, cfg.k)
+    xs = [[G.to_dev(x, "bf16") for x in inp.xs]]
+    dys = [[G.to_dev(g, "bf16") for g in inp.Gs]]
+    ys, dxs = G.run_stage(st, ops, xs, dys, cfg.T, cfg.d, "bf16")
+    kt = {k["name"]: k for k in st.kernel_times()}
+    assert kt["gemm_dh_swiglu_bwd"]["launches"] == cfg.M * cfg.L
+    assert kt["gemm_gateup_swiglu"]["launches"] == cfg.M * cfg.L
+    for name, k in kt.items():
+        assert k["timed"] == -(-k["launches"] // 3), (name, k)
+        assert k["timed"] == 0 or k["total_ms"] > 0, (name, k)
+    again = {k["name"]: k for k in st.kernel_times()}
+    assert again == {}   # totals reset by the report
+    grads = G.stage_grads(st, cfg.L, "swiglu", cfg.d, cfg.f)
+    for i in range(cfg.M):
+        assert np.array_equal(G.to_host(ys[0][i]), ref[0][i]) and np.array_equal(G.to_host(dxs[0][i]), ref[1][i])
+    for blk in range(cfg.L):
+        for key in ref[2][blk]:
+            assert np.array_equal(grads[blk][key], ref[2][blk][key]), key
+    st.close()
