@@ -20,8 +20,11 @@
 // slot), one request per few MFMAs, so each tile has at least a full step to
 // arrive.  The step ends with vmcnt(16) (everything but tile t+2) and a
 // barrier, after which tile t+1's first-half fragments are read under the
-// last 16 MFMAs, in the order a0 b0 a1 b1 ... that the MFMAs consume them
-// (growing squares over the 8 x 8 tiles).  LDS rows are 128 bytes; 16-byte
+// last 16 MFMAs, in the order a0 b0 b1 .. b7 a1 .. a7 that the MFMAs consume
+// them.  The MFMAs of a K half run over the 8 x 8 tiles in serpentine order
+// (rows of j ascending, then descending), so every MFMA shares one operand
+// with the one before it: at the chip's power limit the fewer operand bits
+// that switch, the higher the clock.  LDS rows are 128 bytes; 16-byte
 // chunk c of row r sits at position c ^ ((r >> 1) & 7), which keeps the
 // direct-to-LDS writes and the fragment reads free of bank conflicts.
 //
@@ -151,7 +154,11 @@ template <> struct EpiIn8<EPI_RESID> { uint4 x; };
 template <> struct EpiIn8<EPI_SWIGLU_BWD> { uint4 g, u; };
 template <> struct EpiIn8<EPI_ACC_F32> { float4 c0, c1; };
 
-template <int EPI>
+// fp32 outputs (dn, the weight gradients): the lane's eight columns are two
+// groups of four, 64 columns apart (o0/i0 and o1/i1), so each access
+// instruction covers 256 contiguous bytes of a row.  CHK: an edge tile, where
+// the second group may lie past N (null pointers).
+template <int EPI, bool CHK = false>
 __device__ __forceinline__ void epi_load8(const EpiPtr& a, EpiIn8<EPI>& in) {
     if constexpr (EPI == EPI_RESID) {
         in.x = *reinterpret_cast<const uint4*>(a.i0);
@@ -159,16 +166,16 @@ __device__ __forceinline__ void epi_load8(const EpiPtr& a, EpiIn8<EPI>& in) {
         in.g = *reinterpret_cast<const uint4*>(a.i0);
         in.u = *reinterpret_cast<const uint4*>(a.i1);
     } else if constexpr (EPI == EPI_ACC_F32) {
-        in.c0 = reinterpret_cast<const float4*>(a.i0)[0];
-        in.c1 = reinterpret_cast<const float4*>(a.i0)[1];
+        in.c0 = *reinterpret_cast<const float4*>(a.i0);
+        if (!CHK || a.i1) in.c1 = *reinterpret_cast<const float4*>(a.i1);
     }
 }
 
-template <int EPI>
+template <int EPI, bool CHK = false>
 __device__ __forceinline__ void epi8(const EpiPtr& a, const float (&w)[8], const EpiIn8<EPI>& in) {
     if constexpr (EPI == EPI_STORE_F32) {
-        reinterpret_cast<float4*>(a.o0)[0] = make_float4(w[0], w[1], w[2], w[3]);
-        reinterpret_cast<float4*>(a.o0)[1] = make_float4(w[4], w[5], w[6], w[7]);
+        *reinterpret_cast<float4*>(a.o0) = make_float4(w[0], w[1], w[2], w[3]);
+        if (!CHK || a.o1) *reinterpret_cast<float4*>(a.o1) = make_float4(w[4], w[5], w[6], w[7]);
     } else if constexpr (EPI == EPI_STORE) {
         *reinterpret_cast<uint4*>(a.o0) = pack8(w);
     } else if constexpr (EPI == EPI_RESID) {
@@ -179,8 +186,9 @@ __device__ __forceinline__ void epi8(const EpiPtr& a, const float (&w)[8], const
         *reinterpret_cast<uint4*>(a.o0) = pack8(y);
     } else if constexpr (EPI == EPI_ACC_F32) {
         const float4 c0 = in.c0, c1 = in.c1;
-        reinterpret_cast<float4*>(a.o0)[0] = make_float4(c0.x + w[0], c0.y + w[1], c0.z + w[2], c0.w + w[3]);
-        reinterpret_cast<float4*>(a.o0)[1] = make_float4(c1.x + w[4], c1.y + w[5], c1.z + w[6], c1.w + w[7]);
+        *reinterpret_cast<float4*>(a.o0) = make_float4(c0.x + w[0], c0.y + w[1], c0.z + w[2], c0.w + w[3]);
+        if (!CHK || a.o1)
+            *reinterpret_cast<float4*>(a.o1) = make_float4(c1.x + w[4], c1.y + w[5], c1.z + w[6], c1.w + w[7]);
     }
 }
 
@@ -220,20 +228,13 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
-// MFMA x (0..63) of a K half in growing squares over the 8 x 8 tiles, so the
-// x-th MFMA needs only fragments a[0..m], b[0..m] (read as a0 b0 a1 b1 ...).
-constexpr int ord_i(int x) {
-    int m = 0;
-    while ((m + 1) * (m + 1) <= x) ++m;
-    const int r = x - m * m;
-    return r <= m ? m : r - m - 1;
-}
-constexpr int ord_j(int x) {
-    int m = 0;
-    while ((m + 1) * (m + 1) <= x) ++m;
-    const int r = x - m * m;
-    return r <= m ? r : m;
-}
+// MFMA x (0..63) of a K half in serpentine order over the 8 x 8 tiles: row
+// i = x / 8, columns ascending on even rows and descending on odd ones, so
+// consecutive MFMAs always share one operand.  With fragments read in the
+// order a0 b0 b1 .. b7 a1 .. a7, MFMA x needs only the first
+// min(x + 2, 9 + x / 8) of them.
+constexpr int ord_i(int x) { return x >> 3; }
+constexpr int ord_j(int x) { return ((x >> 3) & 1) ? 7 - (x & 7) : (x & 7); }
 
 // ---- K-contiguous kernel ----------------------------------------------------
 template <int EPI>
@@ -267,9 +268,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     // accumulators of one row are eight consecutive output columns.  SwiGLU
     // (B rows interleaved in groups of 32 gate and 32 up rows): tiles j < 4
     // hold gate row of hidden column 4c + j, tiles j >= 4 the up row of
-    // hidden column 4c + j - 4.
+    // hidden column 4c + j - 4.  fp32 outputs: tiles j < 4 hold B row 4c + j,
+    // tiles j >= 4 B row 64 + 4c + j - 4.
+    constexpr bool F32OUT = EPI == EPI_STORE_F32 || EPI == EPI_ACC_F32;
     auto brow = [&](int row) __attribute__((always_inline)) -> int {
         const int blk = row & ~127, j = (row >> 4) & 7, c = row & 15;
+        if constexpr (F32OUT) return blk + (j >> 2) * 64 + 4 * c + (j & 3);
         if (!p.swiglu) return blk + 8 * c + j;
         const int x = 4 * c + (j & 3);
         return blk + (x >> 5) * 64 + (j >> 2) * 32 + (x & 31);
@@ -312,11 +316,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     const char* fA = smem + (wm * 128 + (lane & 15)) * ROWB;
     const char* fB = smem + (wn * 128 + (lane & 15)) * ROWB;
     bf16x8 fa[2][8], fb[2][8];
-    // fragment x (0..15) of K half s of the tile in slots (sa, sb): a0 b0 a1 b1 ...
+    // fragment x (0..15) of K half s of the tile in slots (sa, sb): a0 b0 b1 .. b7 a1 .. a7
     auto fragx = [&](int sa, int sb, int s, int x, bf16x8 (&a)[8], bf16x8 (&b)[8]) __attribute__((always_inline)) {
-        const int y = x >> 1, pc = s ? pc1 : pc0;
-        if ((x & 1) == 0) a[y] = *reinterpret_cast<const bf16x8*>(fA + sa * OPB + y * 16 * ROWB + pc);
-        else b[y] = *reinterpret_cast<const bf16x8*>(fB + sb * OPB + y * 16 * ROWB + pc);
+        const int pc = s ? pc1 : pc0;
+        if (x == 0 || x >= 9) {
+            const int y = x == 0 ? 0 : x - 8;
+            a[y] = *reinterpret_cast<const bf16x8*>(fA + sa * OPB + y * 16 * ROWB + pc);
+        } else {
+            const int y = x - 1;
+            b[y] = *reinterpret_cast<const bf16x8*>(fB + sb * OPB + y * 16 * ROWB + pc);
+        }
     };
 
     f32x4 acc[8][8];
@@ -420,8 +429,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     // Epilogue.  With the permuted B rows, accumulator register r of tile
     // (i, j) is output row lr + 16i + r, column lc + j: each lane holds eight
     // consecutive columns of a row (SwiGLU: gate tiles j < 4 and up tiles
-    // j >= 4 of the four hidden columns lc .. lc+3).
-    const int lc = p.swiglu ? wn * 64 + 4 * (lane & 15) : wn * 128 + 8 * (lane & 15);
+    // j >= 4 of the four hidden columns lc .. lc+3; fp32 outputs: columns
+    // lc .. lc+3 in tiles j < 4 and lc+64 .. lc+67 in tiles j >= 4).
+    const int lc = p.swiglu || F32OUT ? wn * (p.swiglu ? 64 : 128) + 4 * (lane & 15) : wn * 128 + 8 * (lane & 15);
     // SwiGLU: the RMSNorm factor r of this lane's 32 output rows (the GEMM
     // read x; gamma is folded into B), requested first.
     float rsc[8][4];
@@ -474,8 +484,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
             a.i1 = static_cast<const char*>(e.in1) + ui + li;
         } else if constexpr (EPI == EPI_RESID) {
             a.i0 = static_cast<const char*>(e.in0) + ((int64_t)(i * 16 + r) * e.ldi0 + m0 * e.ldi0 + n0) * 2 + li;
-        } else if constexpr (EPI == EPI_ACC_F32) {
-            a.i0 = o;
+        }
+        if constexpr (F32OUT) a.o1 = o + 64 * ESO;
+        if constexpr (EPI == EPI_ACC_F32) {
+            a.i0 = a.o0;
+            a.i1 = a.o1;
         }
         return a;
     };
@@ -484,9 +497,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
     auto sptr = [&](int64_t row, int64_t col) __attribute__((always_inline)) -> EpiPtr {
         EpiPtr a{};
         a.o0 = static_cast<char*>(e.out0) + (row * e.ld0 + col) * ESO;
-        if constexpr (EPI == EPI_ACC_F32) {
-            if (col >= e.nsplit) a.o0 = static_cast<char*>(e.out1) + (row * e.ld1 + col - e.nsplit) * ESO;
+        if constexpr (F32OUT) {
+            // two groups of four columns, at col and col + 64 (null past N)
+            auto at = [&](int64_t c) __attribute__((always_inline)) -> char* {
+                if (c >= pN) return nullptr;
+                if (EPI == EPI_ACC_F32 && c >= e.nsplit)
+                    return static_cast<char*>(e.out1) + (row * e.ld1 + c - e.nsplit) * ESO;
+                return static_cast<char*>(e.out0) + (row * e.ld0 + c) * ESO;
+            };
+            a.o0 = at(col);
+            a.o1 = at(col + 64);
             a.i0 = a.o0;
+            a.i1 = a.o1;
         } else {
             if constexpr (EPI == EPI_SWIGLU) {
                 a.o1 = static_cast<char*>(e.out1) + (row * e.ld0 + col) * 2;
@@ -520,7 +542,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
             if constexpr (HAS_IN) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (ok(i, r)) epi_load8<EPI>(ptr(i, r), dst[r]);
+                    if (ok(i, r)) epi_load8<EPI, !FAST>(ptr(i, r), dst[r]);
             }
         };
 #pragma unroll
@@ -545,7 +567,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
                     float w[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) w[j] = acc[i][j][r];
-                    if (ok(i, r)) epi8<EPI>(ptr(i, r), w, in[i % NB][r]);
+                    if (ok(i, r)) epi8<EPI, !FAST>(ptr(i, r), w, in[i % NB][r]);
                 }
             }
             if constexpr (EPI == EPI_SWIGLU_BWD && FAST) {
