@@ -36,10 +36,10 @@ PEAK_HBM_GBS = 8000.0
 # copy kernel measured in the same runs).  Valid only for the GEMM source they were taken on.
 TRAFFIC = {
     "config": "c3_80layer_p8_stage0",
-    "gemm_source_sha1": "95e151d505ae61496276f84c441c15f8f645f5d8",
+    "gemm_source_sha1": "077f80009841eb2c33b1951b7127a534f464905b",
     "bytes_per_launch": {
-        "gemm_gateup_swiglu": 13.320e9, "gemm_down_residual": 6.153e9, "gemm_dh_swiglu_bwd": 9.127e9,
-        "gemm_dn": 12.892e9, "gemm_wgrad_down": 8.706e9, "gemm_wgrad_gateup": 8.706e9,
+        "gemm_gateup_swiglu": 13.656e9, "gemm_down_residual": 6.021e9, "gemm_dh_swiglu_bwd": 9.189e9,
+        "gemm_dn": 12.197e9, "gemm_wgrad_down": 8.477e9, "gemm_wgrad_gateup": 8.477e9,
     },
 }
 
