@@ -100,8 +100,9 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
 // ---- epilogue ---------------------------------------------------------------
 // A 16x16 MFMA accumulator gives lane l column l%16 and rows 4*(l/16) + 0..3.
 // With B's rows permuted at load time (see the loader) the columns of a
-// lane's eight tiles j are consecutive output columns, so each lane owns
-// 8-column pieces of rows and every global access is a 16-byte vector.
+// lane's eight tiles j are consecutive output columns (fp32 outputs: two
+// groups of four, 64 columns apart), so every global access is a 16-byte
+// vector and 16 lanes cover 256 contiguous bytes of a row.
 
 __device__ __forceinline__ uint2 pack4(const float (&w)[4]) {
     return make_uint2(pack2_bf(w[0], w[1]), pack2_bf(w[2], w[3]));
