@@ -536,8 +536,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_tn_kernel(const Params p) {
             else return m0 + lr + i * 16 + r < pM && n0 + lc < pN;
         };
         // inputs of row groups i+1 .. i+NB-1 load while row group i computes
-        // (the K loop's fragment registers are free by now)
-        constexpr int NB = EPI == EPI_SWIGLU_BWD ? 4 : EPI == EPI_ACC_F32 ? 3 : 2;
+        // (the K loop's fragment registers are free by now); the fp32
+        // accumulate measured faster one row group ahead than two or three
+        constexpr int NB = EPI == EPI_SWIGLU_BWD ? 4 : 2;
         EpiIn8<EPI> in[NB][4];
         auto prefetch = [&](int i, EpiIn8<EPI> (&dst)[4]) __attribute__((always_inline)) {
             if constexpr (HAS_IN) {
