@@ -33,14 +33,13 @@ PEAK_HBM_GBS = 8000.0
 
 # L2-to-memory bytes per launch of each GEMM role at the c3 workload, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs (bytes = 2.0 x FETCH_SIZE KiB + 1.0 x WRITE_SIZE KiB, scales taken from a plain 1 GiB
-# copy kernel measured in the same runs).  Valid only for the GEMM source they were taken on (taken on
-# sha1 077f80009841eb2c33b1951b7127a534f464905b, which differs from the one below in a comment only).
+# copy kernel measured in the same runs).  Valid only for the GEMM source they were taken on.
 TRAFFIC = {
     "config": "c3_80layer_p8_stage0",
-    "gemm_source_sha1": "68128be91109f9c70451c334a1d3213a627c85b8",
+    "gemm_source_sha1": "a32cc5eebafb6b1c281edeb35e850212196bf1d7",
     "bytes_per_launch": {
-        "gemm_gateup_swiglu": 13.656e9, "gemm_down_residual": 6.021e9, "gemm_dh_swiglu_bwd": 9.189e9,
-        "gemm_dn": 12.197e9, "gemm_wgrad_down": 8.477e9, "gemm_wgrad_gateup": 8.477e9,
+        "gemm_gateup_swiglu": 13.666e9, "gemm_down_residual": 6.052e9, "gemm_dh_swiglu_bwd": 9.170e9,
+        "gemm_dn": 12.631e9, "gemm_wgrad_down": 8.151e9, "gemm_wgrad_gateup": 8.151e9,
     },
 }
 
